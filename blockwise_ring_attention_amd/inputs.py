@@ -1,0 +1,61 @@
+"""Seeded synthetic inputs for a ring member's share.
+
+This module only draws random numbers; it holds no attention arithmetic.  The
+oracle and the GPU path both consume exactly the host tensors it returns.
+
+Each (config, tensor, global block) has its own NumPy stream, so the data of
+a global block does not depend on which member looks at it, and no code path
+ever needs to build the whole sequence in one place.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from .configs import ShareConfig
+
+TENSOR_ID = {"q": 0, "k": 1, "v": 2, "do": 3}
+
+
+def _rng(seed: int, cfg_id: int, tensor: str, block: int) -> np.random.Generator:
+    ss = np.random.SeedSequence(seed, spawn_key=(cfg_id, TENSOR_ID[tensor], block))
+    return np.random.default_rng(ss)
+
+
+def draw(cfg: ShareConfig, tensor: str, block: int, seed: int = 0,
+         length: int | None = None) -> torch.Tensor:
+    """One [B, H, length, d] block of ``tensor`` in the config's dtype (CPU).
+
+    Values are drawn in float32 and rounded to bf16 with round-to-nearest-even
+    for bf16 configs, so both consumers see identical rounded inputs."""
+    L = cfg.block_len if length is None else length
+    shape = (cfg.batch, cfg.heads, L, cfg.head_dim)
+    dist = cfg.dist(tensor)
+    g = _rng(seed, cfg.cfg_id, tensor, block)
+    if dist.kind == "normal":
+        x = g.standard_normal(shape, dtype=np.float32)
+        if dist.scale != 1.0:
+            x *= np.float32(dist.scale)
+    elif dist.kind == "uniform":
+        x = g.random(shape, dtype=np.float32)
+        x *= np.float32(2.0 * dist.scale)
+        x -= np.float32(dist.scale)
+    else:
+        raise ValueError(f"unknown distribution {dist.kind!r}")
+    t = torch.from_numpy(x)
+    if cfg.dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    elif cfg.dtype != "fp32":
+        raise ValueError(f"unknown dtype {cfg.dtype!r}")
+    return t
+
+
+def draw_kv(cfg: ShareConfig, block: int, seed: int = 0) -> torch.Tensor:
+    """Packed key/value block [2, B, H, L, d]: index 0 = K, 1 = V."""
+    k = draw(cfg, "k", block, seed)
+    v = draw(cfg, "v", block, seed)
+    return torch.stack([k, v], dim=0)
+
+
+def torch_dtype(cfg: ShareConfig) -> torch.dtype:
+    return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32

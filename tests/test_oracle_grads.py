@@ -1,0 +1,98 @@
+"""Pins of the oracle's closed-form gradients."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention, attention_grads
+
+
+def _loss(q, k, v, do, qp, kp, causal):
+    o, _ = attention(q, k, v, qp, kp, causal)
+    return float((o * do).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_finite_differences(causal):
+    rng = np.random.default_rng(40)
+    B, H, Lq, Lk, d = 1, 1, 5, 7, 3
+    q = rng.standard_normal((B, H, Lq, d))
+    k = rng.standard_normal((B, H, Lk, d))
+    v = rng.standard_normal((B, H, Lk, d))
+    do = rng.standard_normal((B, H, Lq, d))
+    qp, kp = np.arange(Lq) + 2, np.arange(Lk)
+    dq, dk, dv, _, _ = attention_grads(q, k, v, do, qp, kp, causal)
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            fp = _loss(args["q"], args["k"], args["v"], do, qp, kp, causal)
+            args[name] = xm
+            fm = _loss(args["q"], args["k"], args["v"], do, qp, kp, causal)
+            num[idx] = (fp - fm) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_torch_autograd_fp64(causal):
+    """Independent library route: torch fp64 autograd through the SDPA routine."""
+    rng = np.random.default_rng(41)
+    B, H, L, d = 1, 2, 48, 16
+    arrs = [rng.standard_normal((B, H, L, d)) for _ in range(4)]
+    q, k, v, do = arrs
+    pos = np.arange(L)
+    dq, dk, dv, o, _ = attention_grads(q, k, v, do, pos, pos, causal, row_tile=20)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal)
+    to.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(o, to.detach().numpy(), atol=1e-12)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12)
+
+
+def test_gradient_sum_identities():
+    """sum_j dV_j = sum_i dO_i (rows of P sum to one) and sum_j dK_j = 0 (each
+    row of dS sums to zero over its visible keys), causal mask included."""
+    rng = np.random.default_rng(42)
+    L, d = 64, 8
+    q, k, v, do = (rng.standard_normal((1, 2, L, d)) for _ in range(4))
+    pos = np.arange(L)
+    dq, dk, dv, _, _ = attention_grads(q, k, v, do, pos, pos, True)
+    np.testing.assert_allclose(dv.sum(axis=2), do.sum(axis=2), atol=1e-12)
+    np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12)
+    # shifting every key by a constant does not change dQ
+    c = rng.standard_normal(d)
+    dq2, _, _, _, _ = attention_grads(q, k + c, v, do, pos, pos, True)
+    np.testing.assert_allclose(dq2, dq, atol=1e-11)
+
+
+def test_member_contributions_sum_to_full_gradient():
+    """dK/dV of the whole causal sequence equal the sum over ring members of
+    each member's contribution from its own query rows."""
+    rng = np.random.default_rng(43)
+    N, L, d = 4, 16, 8
+    T = N * L
+    q, k, v, do = (rng.standard_normal((1, 1, T, d)) for _ in range(4))
+    pos = np.arange(T)
+    dq_f, dk_f, dv_f, _, _ = attention_grads(q, k, v, do, pos, pos, True)
+    dk_sum = np.zeros_like(dk_f)
+    dv_sum = np.zeros_like(dv_f)
+    for r in range(N):
+        rows = slice(r * L, (r + 1) * L)
+        dq_r, dk_r, dv_r, _, _ = attention_grads(q[:, :, rows], k, v, do[:, :, rows],
+                                                  pos[rows], pos, True)
+        np.testing.assert_allclose(dq_r, dq_f[:, :, rows], atol=1e-12)
+        if r + 1 < N:                                     # future keys untouched
+            assert np.abs(dk_r[:, :, (r + 1) * L:]).max() == 0.0
+            assert np.abs(dv_r[:, :, (r + 1) * L:]).max() == 0.0
+        dk_sum += dk_r
+        dv_sum += dv_r
+    np.testing.assert_allclose(dk_sum, dk_f, atol=1e-12)
+    np.testing.assert_allclose(dv_sum, dv_f, atol=1e-12)
