@@ -1,0 +1,231 @@
+"""ctypes binding of ``libringattn.so`` (declared in ``include/ring_attn.h``).
+
+Argument marshalling only: every function takes torch CUDA tensors, checks
+that they are contiguous device tensors of the dtype the C ABI expects,
+passes their device pointers, dims and the current HIP stream, and turns a
+negative return code into ``RingAttnError``.  All arithmetic happens in the
+HIP kernels.  There is no fallback: if the library is missing, loading it
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libringattn.so")
+
+RA_BF16, RA_FP32 = 0, 1
+RA_EMU_OVERLAP, RA_EMU_SERIALIZE = 0, 1
+_ERR_NAMES = {-1: "invalid argument", -2: "unsupported", -3: "HIP error"}
+
+
+class RingAttnError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{_ERR_NAMES.get(code, code)}: {message}")
+        self.code = code
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("q_len", ctypes.c_int32), ("kv_len", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+_lib = None
+_lock = threading.Lock()
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_SIGS = {
+    "ring_attn_version": ([], _i),
+    "ring_attn_last_error": ([], ctypes.c_char_p),
+    "ring_attn_init_acc": ([_vp, _vp, ctypes.POINTER(Dims), _vp], _i),
+    "ring_attn_fwd": ([_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, ctypes.POINTER(Dims), _vp], _i),
+    "ring_attn_combine": ([_vp, _vp, _vp, _vp, ctypes.POINTER(Dims), _vp], _i),
+    "ring_attn_finalize": ([_vp, _vp, _i, ctypes.POINTER(Dims), _vp], _i),
+    "ring_attn_bwd_prep": ([_vp, _vp, _vp, ctypes.POINTER(Dims), _vp], _i),
+    "ring_attn_bwd": ([_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp,
+                       ctypes.POINTER(Dims), _vp], _i),
+    "ring_emu_fwd": ([_vp, ctypes.POINTER(_vp), _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp,
+                      ctypes.POINTER(Dims), ctypes.POINTER(ctypes.c_int32), _i, _vp, _vp], _i),
+    "ring_emu_bwd": ([_vp, ctypes.POINTER(_vp), _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(_vp),
+                      _vp, _vp, _i, _i, _i, _i, _i, _vp, ctypes.POINTER(Dims),
+                      ctypes.POINTER(ctypes.c_int32), _i, _vp, _vp], _i),
+}
+EXPORTS = tuple(_SIGS)
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the HIP library once; raise if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise ImportError(
+                f"{p} not found: build the HIP library first "
+                "(python -m blockwise_ring_attention_amd.build)")
+        lib = ctypes.CDLL(p)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def last_error() -> str:
+    return load().ring_attn_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise RingAttnError(rc, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return _vp(t.data_ptr()) if t.numel() else None
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return _vp(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return RA_BF16
+    if t.dtype == torch.float32:
+        return RA_FP32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _need(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def dims(q: torch.Tensor, kv_len: int, scale: float = 0.0) -> Dims:
+    """Dims of a call from the query tensor [B, H, Lq, d] and the block length."""
+    B, H, Lq, d = q.shape
+    return Dims(B, H, Lq, kv_len, d, _dtype_code(q), float(scale))
+
+
+def ring_attn_init_acc(o_acc, lse_acc, scale=0.0, stream=None):
+    _need(o_acc, torch.float32, "o_acc")
+    _need(lse_acc, torch.float32, "lse_acc")
+    B, H, Lq, d = o_acc.shape
+    dm = Dims(B, H, Lq, 0, d, RA_FP32, float(scale))
+    _check(load().ring_attn_init_acc(_ptr(o_acc), _ptr(lse_acc), ctypes.byref(dm), _stream(stream)))
+
+
+def ring_attn_fwd(q, kv_block, ring_rank, ring_step, ring_size, causal, q_chunk, k_chunk,
+                  o_acc, lse_acc, scale=0.0, stream=None):
+    _need(kv_block, q.dtype, "kv_block")
+    _need(o_acc, torch.float32, "o_acc")
+    _need(lse_acc, torch.float32, "lse_acc")
+    dm = dims(q, kv_block.shape[3], scale)
+    _check(load().ring_attn_fwd(_ptr(q), _ptr(kv_block), ring_rank, ring_step, ring_size,
+                                int(bool(causal)), q_chunk, k_chunk, _ptr(o_acc), _ptr(lse_acc),
+                                ctypes.byref(dm), _stream(stream)))
+
+
+def ring_attn_combine(o_a, lse_a, o_b, lse_b, stream=None):
+    for t, n in ((o_a, "o_a"), (lse_a, "lse_a"), (o_b, "o_b"), (lse_b, "lse_b")):
+        _need(t, torch.float32, n)
+    B, H, Lq, d = o_a.shape
+    dm = Dims(B, H, Lq, 0, d, RA_FP32, 0.0)
+    _check(load().ring_attn_combine(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b),
+                                    ctypes.byref(dm), _stream(stream)))
+
+
+def ring_attn_finalize(acc, out, stream=None):
+    _need(acc, torch.float32, "acc")
+    B, H, Lq, d = acc.shape
+    dm = Dims(B, H, Lq, 0, d, RA_FP32, 0.0)
+    _check(load().ring_attn_finalize(_ptr(acc), _ptr(out), _dtype_code(out), ctypes.byref(dm),
+                                     _stream(stream)))
+
+
+def ring_attn_bwd_prep(o, dout, delta, stream=None):
+    _need(o, torch.float32, "o")
+    _need(delta, torch.float32, "delta")
+    dm = dims(dout, 0)
+    _check(load().ring_attn_bwd_prep(_ptr(o), _ptr(dout), _ptr(delta), ctypes.byref(dm),
+                                     _stream(stream)))
+
+
+def ring_attn_bwd(q, kv_block, dout, lse, delta, ring_rank, ring_step, ring_size, causal,
+                  q_chunk, k_chunk, dq_acc, dkv_io, scale=0.0, stream=None):
+    _need(kv_block, q.dtype, "kv_block")
+    _need(dout, q.dtype, "dout")
+    for t, n in ((lse, "lse"), (delta, "delta"), (dq_acc, "dq_acc"), (dkv_io, "dkv_io")):
+        _need(t, torch.float32, n)
+    dm = dims(q, kv_block.shape[3], scale)
+    _check(load().ring_attn_bwd(_ptr(q), _ptr(kv_block), _ptr(dout), _ptr(lse), _ptr(delta),
+                                ring_rank, ring_step, ring_size, int(bool(causal)), q_chunk,
+                                k_chunk, _ptr(dq_acc), _ptr(dkv_io), ctypes.byref(dm),
+                                _stream(stream)))
+
+
+def _ptr_array(ts: Sequence[Optional[torch.Tensor]]):
+    arr = (_vp * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = t.data_ptr() if t is not None else None
+    return arr
+
+
+def _order_array(order):
+    if order is None:
+        return None
+    arr = (ctypes.c_int32 * len(order))(*[int(x) for x in order])
+    return arr
+
+
+def ring_emu_fwd(q, kv_pool, slots, ring_rank, ring_size, causal, q_chunk, k_chunk, o_acc,
+                 lse_acc, scale=0.0, order=None, serialize=False, main_stream=None,
+                 side_stream=None):
+    """kv_pool: list of ring_size packed blocks (None where never needed);
+    slots: two receive buffers shaped like one block."""
+    if len(kv_pool) != ring_size:
+        raise ValueError("kv_pool must have ring_size entries")
+    ref = next(t for t in kv_pool if t is not None)
+    dm = dims(q, ref.shape[3], scale)
+    main = main_stream if main_stream is not None else torch.cuda.current_stream()
+    side = side_stream if side_stream is not None else main
+    _check(load().ring_emu_fwd(_ptr(q), _ptr_array(kv_pool), _ptr(slots[0]), _ptr(slots[1]),
+                               ring_rank, ring_size, int(bool(causal)), q_chunk, k_chunk,
+                               _ptr(o_acc), _ptr(lse_acc), ctypes.byref(dm), _order_array(order),
+                               RA_EMU_SERIALIZE if serialize else RA_EMU_OVERLAP,
+                               _vp(main.cuda_stream), _vp(side.cuda_stream)))
+
+
+def ring_emu_bwd(q, kv_pool, slots, dout, lse, delta, dkv_pool, dkv_slots, ring_rank, ring_size,
+                 causal, q_chunk, k_chunk, dq_acc, scale=0.0, order=None, serialize=False,
+                 main_stream=None, side_stream=None):
+    if len(kv_pool) != ring_size or len(dkv_pool) != ring_size:
+        raise ValueError("pools must have ring_size entries")
+    ref = next(t for t in kv_pool if t is not None)
+    dm = dims(q, ref.shape[3], scale)
+    main = main_stream if main_stream is not None else torch.cuda.current_stream()
+    side = side_stream if side_stream is not None else main
+    _check(load().ring_emu_bwd(_ptr(q), _ptr_array(kv_pool), _ptr(slots[0]), _ptr(slots[1]),
+                               _ptr(dout), _ptr(lse), _ptr(delta), _ptr_array(dkv_pool),
+                               _ptr(dkv_slots[0]), _ptr(dkv_slots[1]), ring_rank, ring_size,
+                               int(bool(causal)), q_chunk, k_chunk, _ptr(dq_acc),
+                               ctypes.byref(dm), _order_array(order),
+                               RA_EMU_SERIALIZE if serialize else RA_EMU_OVERLAP,
+                               _vp(main.cuda_stream), _vp(side.cuda_stream)))

@@ -1,0 +1,254 @@
+// C ABI of the ring-attention library: argument validation, the ring
+// schedule (which block a member holds at a step, and whether the causal
+// mask hides it), and kernel dispatch.  No exception crosses this boundary
+// and nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "ra_api_internal.h"
+#include "ra_common.h"
+#include "ring_attn.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+}  // namespace
+
+int ra_fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ra_hip_fail(hipError_t e, const char* what) {
+  return ra_fail(RA_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const char* pa = (const char*)a;
+  const char* pb = (const char*)b;
+  return pa < pb + nb && pb < pa + na;
+}
+
+int ra_check_dims(const ra_dims* d, ra_shape* s) {
+  if (!d) return ra_fail(RA_ERR_INVALID, "dims is NULL");
+  if (d->batch < 0 || d->heads < 0 || d->q_len < 0 || d->kv_len < 0)
+    return ra_fail(RA_ERR_INVALID, "negative size in dims (B=%d H=%d Lq=%d Lk=%d)",
+                   d->batch, d->heads, d->q_len, d->kv_len);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return ra_fail(RA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
+  if (d->dtype != RA_BF16 && d->dtype != RA_FP32)
+    return ra_fail(RA_ERR_UNSUPPORTED, "dtype %d not supported", d->dtype);
+  if (!isfinite(d->scale)) return ra_fail(RA_ERR_INVALID, "scale is not finite");
+  s->B = d->batch;
+  s->H = d->heads;
+  s->Lq = d->q_len;
+  s->Lk = d->kv_len;
+  s->D = d->head_dim;
+  s->dtype = d->dtype;
+  s->elem = d->dtype == RA_BF16 ? 2 : 4;
+  s->scale = d->scale != 0.f ? d->scale : 1.0f / sqrtf((float)d->head_dim);
+  s->bh = (int64_t)s->B * s->H;
+  s->q_rows = s->bh * s->Lq;
+  s->kv_rows = s->bh * s->Lk;
+  // every row index handled by a kernel must fit a 32-bit grid
+  if (s->q_rows > (int64_t)1 << 40 || s->kv_rows > (int64_t)1 << 40 ||
+      (s->bh > 0 && (s->Lq > (1 << 30) || s->Lk > (1 << 30))))
+    return ra_fail(RA_ERR_INVALID, "problem too large");
+  if (s->bh * ((int64_t)s->Lq + 127) / 128 > 0x7fffffffLL ||
+      s->bh * ((int64_t)s->Lk + 127) / 128 > 0x7fffffffLL)
+    return ra_fail(RA_ERR_INVALID, "problem too large for one launch");
+  return RA_OK;
+}
+
+int ra_check_ring(int rank, int step, int size, int causal, int q_chunk,
+                  int k_chunk, const ra_shape& s) {
+  if (size < 1) return ra_fail(RA_ERR_INVALID, "ring_size %d < 1", size);
+  if (rank < 0 || rank >= size)
+    return ra_fail(RA_ERR_INVALID, "ring_rank %d outside [0, %d)", rank, size);
+  if (step < 0 || step >= size)
+    return ra_fail(RA_ERR_INVALID, "ring_step %d outside [0, %d)", step, size);
+  if (q_chunk < 1 || k_chunk < 1)
+    return ra_fail(RA_ERR_INVALID, "q_chunk %d / k_chunk %d must be >= 1", q_chunk, k_chunk);
+  if (causal && s.Lq != s.Lk)
+    return ra_fail(RA_ERR_INVALID,
+                   "causal ring step needs equal blocks (Lq %d != Lk %d)", s.Lq, s.Lk);
+  return RA_OK;
+}
+
+int ra_block_of_step(int rank, int step, int size) {
+  int kb = (rank - step) % size;
+  return kb < 0 ? kb + size : kb;
+}
+
+int ra_fwd_block(const void* q, const void* kv, int kb, int rank, int causal,
+                 int q_chunk, int k_chunk, float* o_acc, float* lse_acc,
+                 const ra_shape& s, hipStream_t stream) {
+  if (s.q_rows == 0 || s.Lk == 0) return RA_OK;  // empty block: identity
+  if (causal && kb > rank) return RA_OK;         // entirely in the future
+  ra_launch L{s.B, s.H, s.Lq, s.Lk, s.D, s.scale, causal && kb == rank ? 1 : 0,
+              q_chunk, k_chunk, stream};
+  hipError_t e = s.dtype == RA_BF16
+                     ? ra_launch_fwd_bf16(q, kv, o_acc, lse_acc, L)
+                     : ra_launch_fwd_fp32((const float*)q, (const float*)kv, o_acc, lse_acc, L);
+  return e == hipSuccess ? RA_OK : ra_hip_fail(e, "forward kernel launch");
+}
+
+int ra_bwd_block(const void* q, const void* kv, const void* dout, const float* lse,
+                 const float* delta, int kb, int rank, int causal, int q_chunk,
+                 int k_chunk, float* dq_acc, float* dkv, const ra_shape& s,
+                 hipStream_t stream) {
+  if (s.q_rows == 0 || s.Lk == 0) return RA_OK;
+  if (causal && kb > rank) return RA_OK;
+  ra_launch L{s.B, s.H, s.Lq, s.Lk, s.D, s.scale, causal && kb == rank ? 1 : 0,
+              q_chunk, k_chunk, stream};
+  hipError_t e = ra_launch_bwd_bf16(q, kv, dout, lse, delta, dq_acc, dkv, L);
+  return e == hipSuccess ? RA_OK : ra_hip_fail(e, "backward kernel launch");
+}
+
+int ra_check_fwd_buffers(const void* q, const void* kv, const float* o_acc,
+                         const float* lse_acc, const ra_shape& s) {
+  if (s.q_rows == 0) return RA_OK;
+  if (!q || !o_acc || !lse_acc || (s.Lk > 0 && !kv))
+    return ra_fail(RA_ERR_INVALID, "NULL tensor pointer");
+  const size_t qb = (size_t)s.q_rows * s.D * s.elem;
+  const size_t kvb = (size_t)2 * s.kv_rows * s.D * s.elem;
+  const size_t ob = (size_t)s.q_rows * s.D * 4;
+  const size_t lb = (size_t)s.q_rows * 4;
+  if (overlaps(o_acc, ob, q, qb) || overlaps(o_acc, ob, kv, kvb) ||
+      overlaps(lse_acc, lb, q, qb) || overlaps(lse_acc, lb, kv, kvb) ||
+      overlaps(lse_acc, lb, o_acc, ob))
+    return ra_fail(RA_ERR_INVALID, "accumulators overlap an input or each other");
+  return RA_OK;
+}
+
+int ra_check_bwd_buffers(const void* q, const void* kv, const void* dout,
+                         const float* lse, const float* delta, const float* dq,
+                         const float* dkv, const ra_shape& s) {
+  if (s.q_rows == 0) return RA_OK;
+  if (!q || !dout || !lse || !delta || !dq || (s.Lk > 0 && (!kv || !dkv)))
+    return ra_fail(RA_ERR_INVALID, "NULL tensor pointer");
+  const size_t qb = (size_t)s.q_rows * s.D * s.elem;
+  const size_t kvb = (size_t)2 * s.kv_rows * s.D * s.elem;
+  const size_t dqb = (size_t)s.q_rows * s.D * 4;
+  const size_t dkvb = (size_t)2 * s.kv_rows * s.D * 4;
+  const size_t lb = (size_t)s.q_rows * 4;
+  const void* ins[5] = {q, kv, dout, lse, delta};
+  const size_t insz[5] = {qb, kvb, qb, lb, lb};
+  for (int i = 0; i < 5; ++i)
+    if (overlaps(dq, dqb, ins[i], insz[i]) || overlaps(dkv, dkvb, ins[i], insz[i]))
+      return ra_fail(RA_ERR_INVALID, "a gradient output overlaps an input");
+  if (overlaps(dq, dqb, dkv, dkvb))
+    return ra_fail(RA_ERR_INVALID, "dq_acc overlaps dkv_io");
+  return RA_OK;
+}
+
+extern "C" {
+
+int ring_attn_version(void) { return 100; }
+
+const char* ring_attn_last_error(void) { return g_last_error.c_str(); }
+
+int ring_attn_init_acc(float* o_acc, float* lse_acc, const ra_dims* dims, void* stream) {
+  ra_shape s;
+  int rc = ra_check_dims(dims, &s);
+  if (rc) return rc;
+  if (s.q_rows == 0) return RA_OK;
+  if (!o_acc || !lse_acc) return ra_fail(RA_ERR_INVALID, "NULL accumulator");
+  if (overlaps(o_acc, (size_t)s.q_rows * s.D * 4, lse_acc, (size_t)s.q_rows * 4))
+    return ra_fail(RA_ERR_INVALID, "o_acc overlaps lse_acc");
+  hipError_t e = ra_launch_init_acc(o_acc, lse_acc, s.q_rows, s.D, (hipStream_t)stream);
+  return e == hipSuccess ? RA_OK : ra_hip_fail(e, "init kernel launch");
+}
+
+int ring_attn_fwd(const void* q, const void* kv_block, int ring_rank, int ring_step,
+                  int ring_size, int causal, int q_chunk, int k_chunk, float* o_acc,
+                  float* lse_acc, const ra_dims* dims, void* stream) {
+  ra_shape s;
+  int rc = ra_check_dims(dims, &s);
+  if (rc) return rc;
+  if ((rc = ra_check_ring(ring_rank, ring_step, ring_size, causal, q_chunk, k_chunk, s)))
+    return rc;
+  if ((rc = ra_check_fwd_buffers(q, kv_block, o_acc, lse_acc, s))) return rc;
+  const int kb = ra_block_of_step(ring_rank, ring_step, ring_size);
+  return ra_fwd_block(q, kv_block, kb, ring_rank, causal, q_chunk, k_chunk, o_acc,
+                      lse_acc, s, (hipStream_t)stream);
+}
+
+int ring_attn_combine(float* o_a, float* lse_a, const float* o_b, const float* lse_b,
+                      const ra_dims* dims, void* stream) {
+  ra_shape s;
+  int rc = ra_check_dims(dims, &s);
+  if (rc) return rc;
+  if (s.q_rows == 0) return RA_OK;
+  if (!o_a || !lse_a || !o_b || !lse_b) return ra_fail(RA_ERR_INVALID, "NULL tensor pointer");
+  const size_t ob = (size_t)s.q_rows * s.D * 4, lb = (size_t)s.q_rows * 4;
+  if (overlaps(o_a, ob, o_b, ob) || overlaps(o_a, ob, lse_b, lb) ||
+      overlaps(lse_a, lb, o_b, ob) || overlaps(lse_a, lb, lse_b, lb) ||
+      overlaps(o_a, ob, lse_a, lb))
+    return ra_fail(RA_ERR_INVALID, "partials a and b overlap");
+  hipError_t e = ra_launch_combine(o_a, lse_a, o_b, lse_b, s.q_rows, s.D, (hipStream_t)stream);
+  return e == hipSuccess ? RA_OK : ra_hip_fail(e, "combine kernel launch");
+}
+
+int ring_attn_finalize(const float* acc, void* out, int out_dtype, const ra_dims* dims,
+                       void* stream) {
+  ra_shape s;
+  int rc = ra_check_dims(dims, &s);
+  if (rc) return rc;
+  if (out_dtype != RA_BF16 && out_dtype != RA_FP32)
+    return ra_fail(RA_ERR_UNSUPPORTED, "out_dtype %d not supported", out_dtype);
+  if (s.q_rows == 0) return RA_OK;
+  if (!acc || !out) return ra_fail(RA_ERR_INVALID, "NULL tensor pointer");
+  const size_t n = (size_t)s.q_rows * s.D;
+  if (overlaps(acc, n * 4, out, n * (out_dtype == RA_BF16 ? 2 : 4)))
+    return ra_fail(RA_ERR_INVALID, "out overlaps acc");
+  hipError_t e = ra_launch_finalize(acc, out, out_dtype == RA_BF16 ? 0 : 1, (int64_t)n,
+                                    (hipStream_t)stream);
+  return e == hipSuccess ? RA_OK : ra_hip_fail(e, "finalize kernel launch");
+}
+
+int ring_attn_bwd_prep(const float* o, const void* dout, float* delta, const ra_dims* dims,
+                       void* stream) {
+  ra_shape s;
+  int rc = ra_check_dims(dims, &s);
+  if (rc) return rc;
+  if (s.q_rows == 0) return RA_OK;
+  if (!o || !dout || !delta) return ra_fail(RA_ERR_INVALID, "NULL tensor pointer");
+  if (overlaps(delta, (size_t)s.q_rows * 4, o, (size_t)s.q_rows * s.D * 4) ||
+      overlaps(delta, (size_t)s.q_rows * 4, dout, (size_t)s.q_rows * s.D * s.elem))
+    return ra_fail(RA_ERR_INVALID, "delta overlaps an input");
+  hipError_t e = ra_launch_bwd_prep(o, dout, s.dtype == RA_BF16 ? 0 : 1, delta, s.q_rows,
+                                    s.D, (hipStream_t)stream);
+  return e == hipSuccess ? RA_OK : ra_hip_fail(e, "bwd_prep kernel launch");
+}
+
+int ring_attn_bwd(const void* q, const void* kv_block, const void* dout, const float* lse,
+                  const float* delta, int ring_rank, int ring_step, int ring_size,
+                  int causal, int q_chunk, int k_chunk, float* dq_acc, float* dkv_io,
+                  const ra_dims* dims, void* stream) {
+  ra_shape s;
+  int rc = ra_check_dims(dims, &s);
+  if (rc) return rc;
+  if (s.dtype != RA_BF16)
+    return ra_fail(RA_ERR_UNSUPPORTED, "backward is implemented for bf16 inputs only");
+  if ((rc = ra_check_ring(ring_rank, ring_step, ring_size, causal, q_chunk, k_chunk, s)))
+    return rc;
+  if ((rc = ra_check_bwd_buffers(q, kv_block, dout, lse, delta, dq_acc, dkv_io, s)))
+    return rc;
+  const int kb = ra_block_of_step(ring_rank, ring_step, ring_size);
+  return ra_bwd_block(q, kv_block, dout, lse, delta, kb, ring_rank, causal, q_chunk,
+                      k_chunk, dq_acc, dkv_io, s, (hipStream_t)stream);
+}
+
+}  // extern "C"

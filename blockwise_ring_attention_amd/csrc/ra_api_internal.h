@@ -1,0 +1,37 @@
+// Host-side helpers shared by the C ABI and the ring emulator.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ring_attn.h"
+
+// Validated, resolved shape of one call.
+struct ra_shape {
+  int B, H, Lq, Lk, D, dtype, elem;
+  float scale;
+  int64_t bh, q_rows, kv_rows;
+};
+
+int ra_fail(int code, const char* fmt, ...);
+int ra_hip_fail(hipError_t e, const char* what);
+int ra_check_dims(const ra_dims* d, ra_shape* s);
+int ra_check_ring(int rank, int step, int size, int causal, int q_chunk, int k_chunk,
+                  const ra_shape& s);
+int ra_block_of_step(int rank, int step, int size);
+int ra_check_fwd_buffers(const void* q, const void* kv, const float* o_acc,
+                         const float* lse_acc, const ra_shape& s);
+int ra_check_bwd_buffers(const void* q, const void* kv, const void* dout,
+                         const float* lse, const float* delta, const float* dq,
+                         const float* dkv, const ra_shape& s);
+// Attend to block kb and fold (forward) / accumulate gradients (backward).
+// A block in the causal future, an empty block or an empty query set is a
+// no-op.  Arguments are assumed validated.
+int ra_fwd_block(const void* q, const void* kv, int kb, int rank, int causal,
+                 int q_chunk, int k_chunk, float* o_acc, float* lse_acc,
+                 const ra_shape& s, hipStream_t stream);
+int ra_bwd_block(const void* q, const void* kv, const void* dout, const float* lse,
+                 const float* delta, int kb, int rank, int causal, int q_chunk,
+                 int k_chunk, float* dq_acc, float* dkv, const ra_shape& s,
+                 hipStream_t stream);

@@ -1,0 +1,101 @@
+// Internal helpers shared by the HIP sources of the ring-attention library.
+// gfx950 only: 64-lane waves, bf16 MFMA 32x32x16, LDS transpose reads,
+// permlane32 swaps.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Finite "minus infinity" for running maxima: exp2(s - m) stays 0 for masked
+// scores (s = -inf) and no (-inf) - (-inf) is ever formed.
+constexpr float kNegBig = -1.0e30f;
+
+// D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16).
+// Lane l supplies A[l%32][8*(l/32) + i] and B[8*(l/32) + i][l%32], i = 0..7;
+// it receives D[8*(r/4) + 4*(l/32) + r%4][l%32] in register r = 0..15.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives element i%4 of the 8-byte chunk addressed by lane
+// 4*t + i/4, for t = 0..3.  If lane j of the group addresses row (r0 + j/4),
+// columns (c0 + 4*(j%4)) .. +3 of a row-major 16-bit matrix, lane i receives
+// column c0 + i of rows r0 .. r0 + 3: a 4x16 block read transposed.
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Value of x in lane l ^ 32, combined with x by max / add.
+__device__ __forceinline__ float max_halves(float x) {
+  unsigned u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_halves(float x) {
+  unsigned u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Pack registers [8*half, 8*half + 8) of an fp32 accumulator into bf16 (RNE).
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& s, int half) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)s[8 * half + i];
+  return r;
+}
+
+// Workgroup -> tile mapping that keeps consecutive tiles on one XCD.  The
+// dispatcher places workgroup w on XCD w % 8; with this remap XCD x runs the
+// contiguous tile range [x*n/8, (x+1)*n/8), so the workgroups that share a
+// head's key/value block share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int w, int n) {
+  if ((n & 7) != 0) return w;
+  return (w & 7) * (n >> 3) + (w >> 3);
+}
+
+}  // namespace ra
+
+// ---- launchers (host side, defined in the .hip sources) --------------------
+struct ra_launch {
+  int B, H, Lq, Lk, D;
+  float scale;       // resolved (never 0)
+  int diag;          // causal diagonal block: mask key j > query i (local)
+  int q_chunk, k_chunk;
+  hipStream_t stream;
+};
+
+hipError_t ra_launch_fwd_bf16(const void* q, const void* kv, float* o_acc,
+                              float* lse_acc, const ra_launch& a);
+hipError_t ra_launch_fwd_fp32(const float* q, const float* kv, float* o_acc,
+                              float* lse_acc, const ra_launch& a);
+hipError_t ra_launch_init_acc(float* o_acc, float* lse_acc, int64_t rows,
+                              int D, hipStream_t s);
+hipError_t ra_launch_combine(float* o_a, float* lse_a, const float* o_b,
+                             const float* lse_b, int64_t rows, int D,
+                             hipStream_t s);
+hipError_t ra_launch_finalize(const float* acc, void* out, int out_dtype,
+                              int64_t n, hipStream_t s);
+hipError_t ra_launch_bwd_prep(const float* o, const void* dout, int dtype,
+                              float* delta, int64_t rows, int D, hipStream_t s);
+hipError_t ra_launch_bwd_bf16(const void* q, const void* kv, const void* dout,
+                              const float* lse, const float* delta,
+                              float* dq_acc, float* dkv, const ra_launch& a);

@@ -1,0 +1,195 @@
+/*
+ * ring_attn.h -- C ABI for one ring member's share of exact blockwise
+ * softmax attention on AMD Instinct MI355X (gfx950).
+ *
+ * The method (Ring Attention with Blockwise Transformers; "Ring Attention"
+ * and "Blockwise RingAttention" keyword pages, definitions): a sequence is
+ * split into equal contiguous blocks, one per ring member.  A member keeps
+ * its query block while the key/value blocks circulate around the ring; each
+ * arriving block is attended blockwise and folded into a running result.
+ * The fold is the associative online-softmax combine of partial attentions,
+ * and the causal mask and softmax denominator are applied exactly across
+ * block and chunk seams (darcstar research page, commentary).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers on the current HIP device.  The
+ *   caller allocates and frees every buffer; the library allocates no device
+ *   memory.  All work is enqueued asynchronously on the given hipStream_t
+ *   (passed as void*; NULL = the null stream); a device fault surfaces at the
+ *   caller's next synchronisation.
+ * - Layouts are dense row-major, no strides:
+ *     q, dout          [B, H, Lq, d]      (dtype of ra_dims.dtype)
+ *     kv_block         [2, B, H, Lk, d]   (index 0 = K, 1 = V; one copy moves it)
+ *     o_acc, dq_acc    [B, H, Lq, d]      float32
+ *     lse_acc, delta   [B, H, Lq]         float32
+ *     dkv_io           [2, B, H, Lk, d]   float32 (0 = dK, 1 = dV)
+ * - Positions are global: member r's query i sits at r*Lq + i and key j of
+ *   block kb at kb*Lk + j.  Under the causal mask key j is visible to query
+ *   i iff its position is <= the query's (the diagonal is visible).  Causal
+ *   calls therefore require Lq == Lk (equal blocks).
+ * - Ring schedule: at ring step s a member of rank r holds block
+ *   kb = (r - s) mod N (it receives from its predecessor; step 0 is its own
+ *   block).  Under the causal mask a block with kb > r is entirely in the
+ *   future: the call is a no-op that launches nothing.
+ * - Scores are scale * <q_i, k_j> with scale = ra_dims.scale, or 1/sqrt(d)
+ *   when ra_dims.scale == 0.  LSE is the natural-log log-sum-exp of the
+ *   scores over the keys a row has seen so far.
+ * - (o_acc, lse_acc) always hold a NORMALISED partial: o over the keys seen
+ *   so far and its LSE.  The empty partial is (0, -inf); initialise with
+ *   ring_attn_init_acc.
+ * - q_chunk / k_chunk are the query and key chunk sizes of the blockwise
+ *   decomposition (sourcepulse project page, Highlighted Details: tuning
+ *   knobs).  They must be >= 1.  They select the kernels' tile shapes and
+ *   never change the result beyond rounding.
+ *
+ * Errors: every entry point returns RA_OK (0) or a negative code, and never
+ * throws.  Invalid arguments and unsupported shapes are detected on the host
+ * before anything is enqueued; ring_attn_last_error() then returns a
+ * thread-local message describing the most recent failure on this thread.
+ * Calls on different streams may run concurrently from different threads,
+ * provided their output buffers do not overlap.
+ */
+#ifndef RING_ATTN_H
+#define RING_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  RA_OK = 0,
+  RA_ERR_INVALID = -1,      /* null pointer, bad rank/step/size, bad chunk, aliasing */
+  RA_ERR_UNSUPPORTED = -2,  /* head_dim or dtype the kernels do not implement */
+  RA_ERR_HIP = -3           /* a HIP launch or copy failed */
+};
+
+enum { RA_BF16 = 0, RA_FP32 = 1 };
+
+/* Problem shape of one call.  head_dim must be 64 or 128.  batch, heads and
+ * the lengths may be 0 (then the call does nothing and returns RA_OK). */
+typedef struct ra_dims {
+  int32_t batch;
+  int32_t heads;
+  int32_t q_len;     /* Lq: query rows held by the member */
+  int32_t kv_len;    /* Lk: tokens per key/value block */
+  int32_t head_dim;  /* d */
+  int32_t dtype;     /* RA_BF16 or RA_FP32: dtype of q, kv_block and dout */
+  float scale;       /* 0 => 1/sqrt(head_dim) */
+} ra_dims;
+
+/* Version of this ABI (major * 100 + minor). */
+int ring_attn_version(void);
+
+/* Message for the most recent failing call on this thread ("" if none). */
+const char* ring_attn_last_error(void);
+
+/* Set (o_acc, lse_acc) to the empty partial (0, -inf) with a fill kernel
+ * (no hipMemset, so the call may be captured in a HIP graph). */
+int ring_attn_init_acc(float* o_acc, float* lse_acc, const ra_dims* dims,
+                       void* stream);
+
+/* Forward ring step (blockwise pass + fold; Ring Attention keyword page,
+ * definition; darcstar commentary on the associative combine and exact seams).
+ * Attends q to key/value block kb = (ring_rank - ring_step) mod ring_size and
+ * folds the result into (o_acc, lse_acc) in place:
+ *     (o_acc, lse_acc) <- (o_acc, lse_acc) (+) attention(q, kv_block)
+ * where (+) is the combine of ring_attn_combine.  Requirements:
+ * 0 <= ring_rank, ring_step < ring_size; Lq == Lk if causal; o_acc and
+ * lse_acc must not overlap q or kv_block.  A future block under the causal
+ * mask returns RA_OK and leaves the accumulators bitwise unchanged.
+ * bf16 inputs run on bf16 MFMA with fp32 accumulation (the probabilities are
+ * rounded to bf16 before the value product); fp32 inputs run in fp32. */
+int ring_attn_fwd(const void* q, const void* kv_block, int ring_rank,
+                  int ring_step, int ring_size, int causal, int q_chunk,
+                  int k_chunk, float* o_acc, float* lse_acc,
+                  const ra_dims* dims, void* stream);
+
+/* Associative combine of two normalised partials over disjoint key sets
+ * (darcstar commentary: online softmax is associative).  In place on a:
+ *     mu = max(lse_a, lse_b), w_x = exp(lse_x - mu),
+ *     lse_a <- mu + ln(w_a + w_b),  o_a <- (w_a o_a + w_b o_b) / (w_a + w_b)
+ * with (0, -inf) as the identity on either side.  Shapes: o [B,H,Lq,d],
+ * lse [B,H,Lq] (kv_len is ignored).  a and b must not overlap. */
+int ring_attn_combine(float* o_a, float* lse_a, const float* o_b,
+                      const float* lse_b, const ra_dims* dims, void* stream);
+
+/* Cast an fp32 [B, H, Lq, d] accumulator (o_acc or dq_acc) to out_dtype
+ * (RA_BF16 with round-to-nearest-even, or RA_FP32 copy). */
+int ring_attn_finalize(const float* acc, void* out, int out_dtype,
+                       const ra_dims* dims, void* stream);
+
+/* Backward preparation: delta[b,h,i] = sum_c dout[b,h,i,c] * o[b,h,i,c], with
+ * o the final fp32 o_acc of the forward share.  The gradient is that of
+ * sum(dO * O) over the member's rows; the pages do not discuss the backward,
+ * so this follows from the exactness of the forward. */
+int ring_attn_bwd_prep(const float* o, const void* dout, float* delta,
+                       const ra_dims* dims, void* stream);
+
+/* Backward ring step for block kb = (ring_rank - ring_step) mod ring_size.
+ * Recomputes the probabilities from the saved final lse (natural log, as
+ * left in lse_acc by the forward) and accumulates
+ *     dq_acc += dQ  (this block's contribution to the member's dQ)
+ *     dkv_io += [dK_kb, dV_kb]  (this member's contribution to block kb)
+ * so a travelling dK/dV partial can collect every member's contribution.
+ * bf16 only (RA_ERR_UNSUPPORTED for fp32).  A future block under the causal
+ * mask is a no-op.  dq_acc and dkv_io must not overlap each other or any
+ * input. */
+int ring_attn_bwd(const void* q, const void* kv_block, const void* dout,
+                  const float* lse, const float* delta, int ring_rank,
+                  int ring_step, int ring_size, int causal, int q_chunk,
+                  int k_chunk, float* dq_acc, float* dkv_io,
+                  const ra_dims* dims, void* stream);
+
+/* ---- single-GPU ring emulator ------------------------------------------
+ * Plays one member of a ring of ring_size members on one GPU.  The other
+ * members' key/value blocks live in a device pool; the "hop" that would
+ * bring the next block over the interconnect is a device-to-device
+ * hipMemcpyAsync into one of two receive slots, issued on side_stream and
+ * overlapped with the attention of the current block on main_stream
+ * (Ring Attention with Blockwise Transformers, abstract: communication of
+ * key/value blocks overlapped with blockwise computation).  Events order
+ * copy-after-consume and compute-after-copy.  Only two slots exist: there
+ * is never a gather of all blocks.
+ *
+ * kv_pool: HOST array of ring_size device pointers; kv_pool[kb] is block kb
+ *          ([2,B,H,Lk,d]).  Entries that the causal mask never needs (kb >
+ *          ring_rank) may be NULL.  kv_pool[ring_rank] is used in place
+ *          (the member's own block needs no hop).
+ * slots:   two device buffers of one block each.
+ * order:   NULL for the ring schedule, else a HOST array of ring_size block
+ *          ids giving the arrival order (any permutation; the result is
+ *          order-invariant because the combine is commutative).
+ * mode:    RA_EMU_OVERLAP (side-stream copies) or RA_EMU_SERIALIZE (all on
+ *          main_stream; must match OVERLAP bitwise). */
+enum { RA_EMU_OVERLAP = 0, RA_EMU_SERIALIZE = 1 };
+
+int ring_emu_fwd(const void* q, const void* const* kv_pool, void* slot0,
+                 void* slot1, int ring_rank, int ring_size, int causal,
+                 int q_chunk, int k_chunk, float* o_acc, float* lse_acc,
+                 const ra_dims* dims, const int32_t* order, int mode,
+                 void* main_stream, void* side_stream);
+
+/* Backward share through the emulator.  For each step the block's travelling
+ * dK/dV partial dkv_pool[kb] (fp32 [2,B,H,Lk,d], device) is brought into a
+ * receive slot with the key/value block, this member's contribution is added
+ * there, and the slot is copied back to dkv_pool[kb] (the hop to the next
+ * member), so on return dkv_pool[kb] += this member's dK/dV for every block
+ * it sees, in ring order.  dq_acc += the member's dQ.  dkv_slot0/1 are two
+ * fp32 device buffers of one dK/dV block each.  lse and delta are those of
+ * the finished forward share (ring_attn_bwd_prep). */
+int ring_emu_bwd(const void* q, const void* const* kv_pool, void* slot0,
+                 void* slot1, const void* dout, const float* lse,
+                 const float* delta, float* const* dkv_pool, float* dkv_slot0,
+                 float* dkv_slot1, int ring_rank, int ring_size, int causal,
+                 int q_chunk, int k_chunk, float* dq_acc, const ra_dims* dims,
+                 const int32_t* order, int mode, void* main_stream,
+                 void* side_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RING_ATTN_H */

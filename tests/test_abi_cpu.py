@@ -1,0 +1,115 @@
+"""The C ABI library loads, exports every function ``include/ring_attn.h``
+declares, and rejects invalid arguments on the host (no GPU needed: every
+case here fails validation before anything is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from blockwise_ring_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ring_attn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ring_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("HIP library not built")
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("ring_attn_fwd", "ring_attn_combine", "ring_attn_bwd", "ring_attn_bwd_prep",
+              "ring_attn_finalize", "ring_attn_init_acc", "ring_attn_last_error",
+              "ring_attn_version", "ring_emu_fwd", "ring_emu_bwd"):
+        assert n in names
+    assert sorted(_lib.EXPORTS) == names, "binding and header disagree"
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert lib.ring_attn_version() == 100
+    assert lib.ring_attn_last_error() == b""
+
+
+def _dims(**kw):
+    base = dict(batch=1, heads=2, q_len=64, kv_len=64, head_dim=128, dtype=0, scale=0.0)
+    base.update(kw)
+    return _lib.Dims(*base.values())
+
+
+FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
+FAKE2 = ctypes.c_void_p(0x100000)
+
+
+def _fwd(lib, dims, rank=0, step=0, size=1, causal=1, qc=64, kc=64, q=FAKE, kv=FAKE2,
+         o=ctypes.c_void_p(0x10000000), lse=ctypes.c_void_p(0x20000000)):
+    return lib.ring_attn_fwd(q, kv, rank, step, size, causal, qc, kc, o, lse,
+                             ctypes.byref(dims) if dims is not None else None, None)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(dims=None), -1),
+    (dict(rank=2, size=2), -1),
+    (dict(rank=-1, size=2), -1),
+    (dict(step=3, size=3), -1),
+    (dict(size=0), -1),
+    (dict(qc=0), -1),
+    (dict(kc=-4), -1),
+    (dict(q=None), -1),
+    (dict(o=ctypes.c_void_p(0x1000)), -1),             # o_acc aliases q
+])
+def test_invalid_arguments_rejected(lib, case, code):
+    dims = case.pop("dims", _dims())
+    assert _fwd(lib, dims, **case) == code
+    assert lib.ring_attn_last_error() != b""
+
+
+def test_unsupported_and_invalid_dims(lib):
+    assert _fwd(lib, _dims(head_dim=96)) == -2
+    assert _fwd(lib, _dims(dtype=7)) == -2
+    assert _fwd(lib, _dims(batch=-1)) == -1
+    assert _fwd(lib, _dims(q_len=64, kv_len=32)) == -1           # causal needs equal blocks
+    assert _fwd(lib, _dims(scale=float("inf"))) == -1
+    # the backward is bf16-only
+    d = _dims(dtype=1)
+    assert lib.ring_attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, 1, 1, 64, 64, FAKE, FAKE,
+                             ctypes.byref(d), None) == -2
+    assert b"bf16" in lib.ring_attn_last_error()
+
+
+def test_empty_problems_are_no_ops(lib):
+    # nothing to compute: succeeds without touching a pointer or the GPU
+    assert _fwd(lib, _dims(q_len=0, kv_len=0), q=None, kv=None, o=None, lse=None) == 0
+    assert _fwd(lib, _dims(batch=0), q=None, kv=None, o=None, lse=None) == 0
+    d = _dims(heads=0)
+    assert lib.ring_attn_combine(None, None, None, None, ctypes.byref(d), None) == 0
+
+
+def test_emulator_rejects_bad_schedules(lib):
+    d = _dims()
+    pool = (ctypes.c_void_p * 2)(FAKE2.value, 0x300000)
+    bad_order = (ctypes.c_int32 * 2)(0, 0)
+    rc = lib.ring_emu_fwd(FAKE, pool, None, None, 0, 2, 0, 64, 64,
+                          ctypes.c_void_p(0x10000000), ctypes.c_void_p(0x20000000),
+                          ctypes.byref(d), bad_order, 0, None, None)
+    assert rc == -1 and b"permutation" in lib.ring_attn_last_error()
+    rc = lib.ring_emu_fwd(FAKE, pool, None, None, 0, 2, 0, 64, 64,
+                          ctypes.c_void_p(0x10000000), ctypes.c_void_p(0x20000000),
+                          ctypes.byref(d), None, 5, None, None)
+    assert rc == -1 and b"mode" in lib.ring_attn_last_error()
+    # two blocks need a receive slot; none given
+    rc = lib.ring_emu_fwd(FAKE, pool, None, None, 0, 2, 0, 64, 64,
+                          ctypes.c_void_p(0x10000000), ctypes.c_void_p(0x20000000),
+                          ctypes.byref(d), None, 0, None, None)
+    assert rc == -1 and b"slot" in lib.ring_attn_last_error()
