@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Throughput of one ring member's attention share on one MI355X.
+
+Workload: the LWM-7B-shaped causal share (batch 1, 32 heads, head_dim 128,
+bf16, ring of 8, the last member: 16384 local queries against 131072 keys).
+One step is the whole hot path: initialise the accumulators, fold the 8
+key/value blocks in ring order through the single-GPU ring emulator (each
+hop a device-to-device copy on a side stream, overlapped with compute),
+cast the output to bf16, then the backward share (row dot products, then the
+8 blocks again, each block's dK/dV partial received, accumulated and sent
+on).  Inputs are resident in HBM before the timed region starts.
+
+Throughput is causal-adjusted: 4*d flops per unmasked (query, key) pair for
+the forward and 10*d for the backward (which recomputes the scores), over
+r*L^2 + L(L+1)/2 pairs per head for member r with blocks of L tokens.
+
+Prints one JSON line.  ``--gpus`` above 1 is refused: this benchmark runs one
+member's share on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+METRIC = "causal-adjusted attention TFLOP/s per GPU (fwd, fwd+bwd); % of bf16 MFMA peak"
+FWD_FLOPS_PER_PAIR_PER_D = 4
+BWD_FLOPS_PER_PAIR_PER_D = 10
+# Products each kernel family forms per unmasked pair, in units of d flops:
+# forward S and PV; the backward's query-major dQ kernel forms S, dP and dQ,
+# its key-major dK/dV kernel forms S, dP, dV and dK.
+KERNEL_FLOPS_PER_PAIR_PER_D = {"fwd_bf16": 4, "bwd_dq": 6, "bwd_dkv": 8}
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target duration of the oracle's timed CPU sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-phases", action="store_true",
+                    help="skip the separate forward-only / backward-only timings")
+    return ap.parse_args()
+
+
+def _cpu_baseline(host, cfg, rank, target_s):
+    """The fp64 oracle, as it stands, on a bounded sample of the same share:
+    the last rows of some heads (rows that see every past block and nearly
+    all of the diagonal block), forward + gradients."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    L = cfg.block_len
+    blocks = sorted(host.kv)
+    k_pos = np.concatenate([oracle.positions(b, L) for b in blocks])
+
+    def run(heads, nrows):
+        rows = np.arange(L - nrows, L)
+        q_pos = oracle.positions(rank, L)[rows]
+        pairs = 0
+        t0 = time.perf_counter()
+        for h in heads:
+            k = torch.cat([host.kv[b][0][:, h:h + 1] for b in blocks], dim=2)
+            v = torch.cat([host.kv[b][1][:, h:h + 1] for b in blocks], dim=2)
+            q = host.q[:, h:h + 1, rows]
+            do = host.dout[:, h:h + 1, rows]
+            oracle.attention_grads(q, k, v, do, q_pos, k_pos, cfg.causal)
+            pairs += int(sum(int((k_pos <= p).sum()) for p in q_pos)) * cfg.batch
+        return time.perf_counter() - t0, pairs
+
+    nrows = 256
+    dt, pairs = run([0], nrows)
+    heads = 1
+    if dt < target_s:
+        heads = int(min(cfg.heads, max(1, round(target_s / max(dt, 1e-3)))))
+        dt, pairs = run(list(range(heads)), nrows)
+    flops = (FWD_FLOPS_PER_PAIR_PER_D + BWD_FLOPS_PER_PAIR_PER_D) * cfg.head_dim * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"fp64 oracle forward + gradients for the last {nrows} query rows of "
+                       f"{heads} head(s) against all {len(k_pos)} keys ({pairs} unmasked pairs), "
+                       f"{dt:.1f} s"),
+            "seconds": round(dt, 2)}
+
+
+def main():
+    args = _parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one ring member's share on one GPU; --gpus {args.gpus} "
+              f"(WORLD_SIZE {world}) is not supported: the multi-GPU ring is not part of this "
+              "build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from blockwise_ring_attention_amd import _lib, share
+    from blockwise_ring_attention_amd.configs import CONFIGS, scaled
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    _lib.load()
+    cfg = scaled(CONFIGS[3], backward=True)
+    rank = cfg.ranks[0]
+    t_gen = time.perf_counter()
+    host = share.make_host_share(cfg, rank, seed=0, backward=True)
+    dev = share.upload(host)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    main_stream = torch.cuda.current_stream()
+    side = share.side_stream_for(dev.q.device)
+
+    def fwd():
+        share.forward(dev, side_stream=side)
+        return share.finalize(dev)
+
+    def bwd():
+        share.backward(dev, side_stream=side)
+
+    def step():
+        fwd()
+        bwd()
+
+    def timed(fn, steps):
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        start.record(main_stream)
+        for _ in range(steps):
+            fn()
+        stop.record(main_stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - w0) * 1e3 / steps
+        return start.elapsed_time(stop) / steps, wall
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    _lib.ring_attn_timing_enable(True)
+    ms_step, wall_step = timed(step, args.steps)
+    _lib.ring_attn_timing_enable(False)
+    kernels = {}
+    for fam in ("fwd_bf16", "bwd_dq", "bwd_dkv"):
+        n, tot = _lib.ring_attn_timing_read(fam)
+        kernels[fam] = {"launches": n, "total_ms": tot}
+
+    pairs = cfg.pairs(rank)
+    d = cfg.head_dim
+    fwd_flops = FWD_FLOPS_PER_PAIR_PER_D * d * pairs
+    bwd_flops = BWD_FLOPS_PER_PAIR_PER_D * d * pairs
+    tflops = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
+
+    phases = {}
+    if not args.no_phases:
+        ms_fwd, _ = timed(fwd, args.steps)
+        ms_bwd, _ = timed(bwd, args.steps)
+        for name, ms, fl in (("fwd", ms_fwd, fwd_flops), ("bwd", ms_bwd, bwd_flops)):
+            tf = fl / (ms * 1e-3) / 1e12
+            phases[name] = {"ms": round(ms, 3), "tflops": round(tf, 1),
+                            "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+    # Roofline of the kernel family that takes the most time in the step.
+    per_kernel = {}
+    for fam, rec in kernels.items():
+        if rec["launches"] == 0:
+            continue
+        flops = KERNEL_FLOPS_PER_PAIR_PER_D[fam] * d * pairs * args.steps
+        avg_ms = rec["total_ms"] / rec["launches"]
+        achieved = flops / (rec["total_ms"] * 1e-3) / 1e12
+        per_kernel[fam] = {"launches": rec["launches"], "avg_ms": round(avg_ms, 4),
+                           "total_ms_per_step": round(rec["total_ms"] / args.steps, 3),
+                           "tflops": round(achieved, 1),
+                           "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    dom = max(per_kernel, key=lambda f: per_kernel[f]["total_ms_per_step"])
+    roofline = {"bound": "mfma", "achieved": per_kernel[dom]["tflops"], "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": per_kernel[dom]["frac"], "traffic": None,
+                "kernel": dom}
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": ("lwm7b-causal-ring-share fwd+bwd: batch 1, 32 heads, head_dim 128, "
+                                "ring 8, rank 7, 16384 local queries x 131072 keys"),
+                   "batch": cfg.batch, "heads": cfg.heads, "head_dim": d,
+                   "ring_size": cfg.ring_size, "rank": rank, "local_queries": cfg.block_len,
+                   "keys": cfg.block_len * (rank + 1), "causal": cfg.causal,
+                   "q_chunk": cfg.q_chunk, "k_chunk": cfg.k_chunk,
+                   "unmasked_pairs": pairs},
+        "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "wall_ms_per_step": round(wall_step, 3),
+        "phases": phases,
+        "kernels": per_kernel,
+        "roofline": roofline,
+        "input_setup_s": round(t_gen, 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = _cpu_baseline(host, cfg, rank, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -56,6 +56,8 @@ _SIGS = {
     "ring_emu_bwd": ([_vp, ctypes.POINTER(_vp), _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(_vp),
                       _vp, _vp, _i, _i, _i, _i, _i, _vp, ctypes.POINTER(Dims),
                       ctypes.POINTER(ctypes.c_int32), _i, _vp, _vp], _i),
+    "ring_attn_timing_enable": ([_i], _i),
+    "ring_attn_timing_read": ([ctypes.c_char_p, ctypes.POINTER(_i), ctypes.POINTER(ctypes.c_double)], _i),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -229,3 +231,15 @@ def ring_emu_bwd(q, kv_pool, slots, dout, lse, delta, dkv_pool, dkv_slots, ring_
                                ctypes.byref(dm), _order_array(order),
                                RA_EMU_SERIALIZE if serialize else RA_EMU_OVERLAP,
                                _vp(main.cuda_stream), _vp(side.cuda_stream)))
+
+
+def ring_attn_timing_enable(on: bool = True) -> None:
+    _check(load().ring_attn_timing_enable(int(bool(on))))
+
+
+def ring_attn_timing_read(name: str):
+    """(launches, total_ms) of one kernel family since timing was enabled."""
+    n = _i(0)
+    ms = ctypes.c_double(0.0)
+    _check(load().ring_attn_timing_read(name.encode(), ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value

@@ -7,7 +7,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "ra_api_internal.h"
 #include "ra_common.h"
@@ -16,6 +18,62 @@
 namespace {
 
 thread_local std::string g_last_error;
+
+// ---- kernel timing: event pairs around launches, kept until read ---------
+enum Kind { kFwdBf16 = 0, kFwdFp32, kBwdDq, kBwdDkv, kKinds };
+const char* const kKindNames[kKinds] = {"fwd_bf16", "fwd_fp32", "bwd_dq", "bwd_dkv"};
+
+struct TimingRec {
+  int kind;
+  hipEvent_t start, stop;
+};
+
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<TimingRec> g_recs;
+std::vector<hipEvent_t> g_spare;
+
+hipEvent_t take_event() {  // caller holds g_tmu
+  if (!g_spare.empty()) {
+    hipEvent_t e = g_spare.back();
+    g_spare.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Brackets one kernel launch when timing is on; a no-op otherwise.
+class Timed {
+ public:
+  Timed(int kind, hipStream_t s) : kind_(kind), s_(s) {
+    std::lock_guard<std::mutex> g(g_tmu);
+    if (!g_timing) return;
+    start_ = take_event();
+    if (start_ && hipEventRecord(start_, s_) != hipSuccess) {
+      g_spare.push_back(start_);
+      start_ = nullptr;
+    }
+  }
+  void done() {
+    if (!start_) return;
+    std::lock_guard<std::mutex> g(g_tmu);
+    hipEvent_t stop = take_event();
+    if (stop && hipEventRecord(stop, s_) == hipSuccess) {
+      g_recs.push_back({kind_, start_, stop});
+    } else {
+      g_spare.push_back(start_);
+      if (stop) g_spare.push_back(stop);
+    }
+    start_ = nullptr;
+  }
+
+ private:
+  int kind_;
+  hipStream_t s_;
+  hipEvent_t start_ = nullptr;
+};
 
 }  // namespace
 
@@ -98,9 +156,11 @@ int ra_fwd_block(const void* q, const void* kv, int kb, int rank, int causal,
   if (causal && kb > rank) return RA_OK;         // entirely in the future
   ra_launch L{s.B, s.H, s.Lq, s.Lk, s.D, s.scale, causal && kb == rank ? 1 : 0,
               q_chunk, k_chunk, stream};
+  Timed t(s.dtype == RA_BF16 ? kFwdBf16 : kFwdFp32, stream);
   hipError_t e = s.dtype == RA_BF16
                      ? ra_launch_fwd_bf16(q, kv, o_acc, lse_acc, L)
                      : ra_launch_fwd_fp32((const float*)q, (const float*)kv, o_acc, lse_acc, L);
+  t.done();
   return e == hipSuccess ? RA_OK : ra_hip_fail(e, "forward kernel launch");
 }
 
@@ -112,8 +172,14 @@ int ra_bwd_block(const void* q, const void* kv, const void* dout, const float* l
   if (causal && kb > rank) return RA_OK;
   ra_launch L{s.B, s.H, s.Lq, s.Lk, s.D, s.scale, causal && kb == rank ? 1 : 0,
               q_chunk, k_chunk, stream};
-  hipError_t e = ra_launch_bwd_bf16(q, kv, dout, lse, delta, dq_acc, dkv, L);
-  return e == hipSuccess ? RA_OK : ra_hip_fail(e, "backward kernel launch");
+  Timed tq(kBwdDq, stream);
+  hipError_t e = ra_launch_bwd_dq(q, kv, dout, lse, delta, dq_acc, L);
+  tq.done();
+  if (e != hipSuccess) return ra_hip_fail(e, "backward dQ kernel launch");
+  Timed tkv(kBwdDkv, stream);
+  e = ra_launch_bwd_dkv(q, kv, dout, lse, delta, dkv, L);
+  tkv.done();
+  return e == hipSuccess ? RA_OK : ra_hip_fail(e, "backward dK/dV kernel launch");
 }
 
 int ra_check_fwd_buffers(const void* q, const void* kv, const float* o_acc,
@@ -156,6 +222,43 @@ int ra_check_bwd_buffers(const void* q, const void* kv, const void* dout,
 extern "C" {
 
 int ring_attn_version(void) { return 100; }
+
+int ring_attn_timing_enable(int on) {
+  std::lock_guard<std::mutex> g(g_tmu);
+  if (on) {
+    for (const TimingRec& r : g_recs) {
+      (void)hipEventSynchronize(r.stop);
+      g_spare.push_back(r.start);
+      g_spare.push_back(r.stop);
+    }
+    g_recs.clear();
+  }
+  g_timing = on != 0;
+  return RA_OK;
+}
+
+int ring_attn_timing_read(const char* name, int* launches, double* total_ms) {
+  if (!name || !launches || !total_ms) return ra_fail(RA_ERR_INVALID, "NULL argument");
+  int kind = -1;
+  for (int k = 0; k < kKinds; ++k)
+    if (std::string(name) == kKindNames[k]) kind = k;
+  if (kind < 0) return ra_fail(RA_ERR_INVALID, "unknown kernel family '%s'", name);
+  std::lock_guard<std::mutex> g(g_tmu);
+  int n = 0;
+  double total = 0.0;
+  for (const TimingRec& r : g_recs) {
+    if (r.kind != kind) continue;
+    hipError_t e = hipEventSynchronize(r.stop);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess) return ra_hip_fail(e, "reading kernel timing events");
+    ++n;
+    total += ms;
+  }
+  *launches = n;
+  *total_ms = total;
+  return RA_OK;
+}
 
 const char* ring_attn_last_error(void) { return g_last_error.c_str(); }
 

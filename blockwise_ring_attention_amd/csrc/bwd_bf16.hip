@@ -358,34 +358,45 @@ __global__ __launch_bounds__(kNW * 64, 1) void dkv_kernel(
 }
 
 template <int D>
-hipError_t launch_d(const void* q, const void* kv, const void* dout,
-                    const float* lse, const float* delta, float* dq, float* dkv,
-                    const ra_launch& a) {
+hipError_t launch_dq(const void* q, const void* kv, const void* dout, const float* lse,
+                     const float* delta, float* dq, const ra_launch& a) {
   const int BH = a.B * a.H;
-  const float c2 = a.scale * kLog2e;
   constexpr int BM = kNW * 32;
   const int n_qt = (a.Lq + BM - 1) / BM;
-  if ((long long)n_qt * BH > 0)
-    hipLaunchKernelGGL((dq_kernel<D, 64>), dim3(n_qt * BH), dim3(kNW * 64), 0,
-                       a.stream, (const bf16*)q, (const bf16*)kv, (const bf16*)dout,
-                       lse, delta, dq, BH, a.Lq, a.Lk, n_qt, a.diag, c2, a.scale);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if ((long long)n_qt * BH <= 0) return hipSuccess;
+  hipLaunchKernelGGL((dq_kernel<D, 64>), dim3(n_qt * BH), dim3(kNW * 64), 0, a.stream,
+                     (const bf16*)q, (const bf16*)kv, (const bf16*)dout, lse, delta, dq, BH,
+                     a.Lq, a.Lk, n_qt, a.diag, a.scale * kLog2e, a.scale);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dkv(const void* q, const void* kv, const void* dout, const float* lse,
+                      const float* delta, float* dkv, const ra_launch& a) {
+  const int BH = a.B * a.H;
   constexpr int BK = kNW * 32;
   const int n_kt = (a.Lk + BK - 1) / BK;
-  if ((long long)n_kt * BH > 0)
-    hipLaunchKernelGGL((dkv_kernel<D, 64>), dim3(n_kt * BH), dim3(kNW * 64), 0,
-                       a.stream, (const bf16*)q, (const bf16*)kv, (const bf16*)dout,
-                       lse, delta, dkv, BH, a.Lq, a.Lk, n_kt, a.diag, c2, a.scale);
+  if ((long long)n_kt * BH <= 0) return hipSuccess;
+  hipLaunchKernelGGL((dkv_kernel<D, 64>), dim3(n_kt * BH), dim3(kNW * 64), 0, a.stream,
+                     (const bf16*)q, (const bf16*)kv, (const bf16*)dout, lse, delta, dkv, BH,
+                     a.Lq, a.Lk, n_kt, a.diag, a.scale * kLog2e, a.scale);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t ra_launch_bwd_bf16(const void* q, const void* kv, const void* dout,
-                              const float* lse, const float* delta,
-                              float* dq_acc, float* dkv, const ra_launch& a) {
-  if (a.D == 128) return launch_d<128>(q, kv, dout, lse, delta, dq_acc, dkv, a);
-  if (a.D == 64) return launch_d<64>(q, kv, dout, lse, delta, dq_acc, dkv, a);
+hipError_t ra_launch_bwd_dq(const void* q, const void* kv, const void* dout,
+                            const float* lse, const float* delta, float* dq_acc,
+                            const ra_launch& a) {
+  if (a.D == 128) return launch_dq<128>(q, kv, dout, lse, delta, dq_acc, a);
+  if (a.D == 64) return launch_dq<64>(q, kv, dout, lse, delta, dq_acc, a);
+  return hipErrorInvalidValue;
+}
+
+hipError_t ra_launch_bwd_dkv(const void* q, const void* kv, const void* dout,
+                             const float* lse, const float* delta, float* dkv,
+                             const ra_launch& a) {
+  if (a.D == 128) return launch_dkv<128>(q, kv, dout, lse, delta, dkv, a);
+  if (a.D == 64) return launch_dkv<64>(q, kv, dout, lse, delta, dkv, a);
   return hipErrorInvalidValue;
 }

@@ -10,6 +10,9 @@
 // key/value blocks circulate).  Two events per slot order the hazards:
 //   copied[i]   : compute on slot i waits for the copy into it;
 //   consumed[i] : the next copy into slot i waits for the compute reading it.
+// On entry the side stream waits for everything already queued on the main
+// stream, so back-to-back calls (a forward share followed by its backward
+// share, or the next step) never overwrite a slot that is still being read.
 // Only two slots ever exist, so the member never holds the whole sequence
 // (darcstar commentary: an all-gather of every block would discard the
 // method's memory saving).
@@ -23,7 +26,7 @@
 namespace {
 
 struct Events {
-  hipEvent_t e[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+  hipEvent_t e[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   int n = 0;
   int create(int count) {
     for (n = 0; n < count; ++n) {
@@ -99,8 +102,14 @@ extern "C" int ring_emu_fwd(const void* q, const void* const* kv_pool, void* slo
   for (int kb : blocks)
     if (kb != ring_rank) copy_block.push_back(kb);
 
-  Events ev;  // 0,1: copied[slot]; 2,3: consumed[slot]
-  if (mode == RA_EMU_OVERLAP && (rc = ev.create(4))) return rc;
+  Events ev;  // 0,1: copied[slot]; 2,3: consumed[slot]; 4: entry
+  if (mode == RA_EMU_OVERLAP) {
+    if ((rc = ev.create(5))) return rc;
+    // Work already queued on main (an earlier share still reading the slots,
+    // the caller's writes to the pool) precedes every hop of this call.
+    RA_HIP(hipEventRecord(ev.e[4], main), "hipEventRecord");
+    RA_HIP(hipStreamWaitEvent(side, ev.e[4], 0), "hipStreamWaitEvent");
+  }
   auto issue_copy = [&](int ci) -> int {
     const int slot = ci & 1;
     if (mode == RA_EMU_OVERLAP && ci >= 2)
@@ -193,8 +202,12 @@ extern "C" int ring_emu_bwd(const void* q, const void* const* kv_pool, void* slo
   if (mode == RA_EMU_OVERLAP && side == main)
     return ra_fail(RA_ERR_INVALID, "overlap mode needs a side stream distinct from main");
 
-  Events ev;  // 0,1 copied; 2,3 consumed; 4 side done
-  if (mode == RA_EMU_OVERLAP && (rc = ev.create(5))) return rc;
+  Events ev;  // 0,1 copied; 2,3 consumed; 4 side done; 5 entry
+  if (mode == RA_EMU_OVERLAP) {
+    if ((rc = ev.create(6))) return rc;
+    RA_HIP(hipEventRecord(ev.e[5], main), "hipEventRecord");
+    RA_HIP(hipStreamWaitEvent(side, ev.e[5], 0), "hipStreamWaitEvent");
+  }
   // Receive: the key/value block and its travelling dK/dV partial.
   auto issue_in = [&](int ci) -> int {
     const int slot = ci & 1;

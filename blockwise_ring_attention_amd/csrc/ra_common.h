@@ -96,6 +96,9 @@ hipError_t ra_launch_finalize(const float* acc, void* out, int out_dtype,
                               int64_t n, hipStream_t s);
 hipError_t ra_launch_bwd_prep(const float* o, const void* dout, int dtype,
                               float* delta, int64_t rows, int D, hipStream_t s);
-hipError_t ra_launch_bwd_bf16(const void* q, const void* kv, const void* dout,
-                              const float* lse, const float* delta,
-                              float* dq_acc, float* dkv, const ra_launch& a);
+hipError_t ra_launch_bwd_dq(const void* q, const void* kv, const void* dout,
+                            const float* lse, const float* delta, float* dq_acc,
+                            const ra_launch& a);
+hipError_t ra_launch_bwd_dkv(const void* q, const void* kv, const void* dout,
+                             const float* lse, const float* delta, float* dkv,
+                             const ra_launch& a);

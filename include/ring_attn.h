@@ -188,6 +188,18 @@ int ring_emu_bwd(const void* q, const void* const* kv_pool, void* slot0,
                  const int32_t* order, int mode, void* main_stream,
                  void* side_stream);
 
+/* ---- kernel timing (diagnostics) ---------------------------------------
+ * While enabled, each attention kernel the library launches is bracketed by
+ * a pair of HIP events recorded on the stream the kernel runs on.  Kernel
+ * families: "fwd_bf16", "fwd_fp32", "bwd_dq", "bwd_dkv".
+ * ring_attn_timing_enable(on): on != 0 discards earlier records and starts
+ * collecting; 0 stops collecting (records are kept).
+ * ring_attn_timing_read(name, &launches, &total_ms): waits for the recorded
+ * events of that family and returns the launch count and summed durations.
+ * Returns RA_ERR_INVALID for an unknown family or NULL outputs. */
+int ring_attn_timing_enable(int on);
+int ring_attn_timing_read(const char* name, int* launches, double* total_ms);
+
 #ifdef __cplusplus
 }
 #endif

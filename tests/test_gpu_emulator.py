@@ -93,3 +93,27 @@ def test_only_two_receive_slots(host):
     torch.cuda.synchronize()
     assert torch.cuda.memory_allocated() == before
     assert len(dev.slots) == 2
+
+
+def test_back_to_back_shares_do_not_race():
+    """Regression: a backward share enqueued right after the forward share
+    (same receive slots, no host synchronisation) once overwrote slots the
+    forward was still reading.  Short blocks make each compute step brief, so
+    the hops of the next call would land during it.  Every result must equal
+    the fully serialised run bitwise."""
+    cfg = ShareConfig(99, "b2b", "bf16", 1, 4, 128, 4, 2048, (3,), True, 256, 64, backward=True)
+    host = share.make_host_share(cfg, 3, backward=True)
+    ref = share.upload(host)
+    share.forward(ref, serialize=True)
+    share.backward(ref, serialize=True)
+    torch.cuda.synchronize()
+    dev = share.upload(host)
+    for _ in range(2):
+        share.forward(dev)
+        share.backward(dev)
+    share.forward(dev)
+    torch.cuda.synchronize()
+    assert torch.equal(dev.o_acc, ref.o_acc) and torch.equal(dev.lse_acc, ref.lse_acc)
+    assert torch.equal(dev.dq_acc, ref.dq_acc)
+    for a, b in zip(dev.dkv_pool, ref.dkv_pool):
+        assert torch.equal(a, 2 * b)          # two backward shares accumulated
