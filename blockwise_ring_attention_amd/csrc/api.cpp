@@ -107,7 +107,8 @@ int ra_check_dims(const ra_dims* d, ra_shape* s) {
     return ra_fail(RA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
   if (d->dtype != RA_BF16 && d->dtype != RA_FP32)
     return ra_fail(RA_ERR_UNSUPPORTED, "dtype %d not supported", d->dtype);
-  if (!isfinite(d->scale)) return ra_fail(RA_ERR_INVALID, "scale is not finite");
+  if (!isfinite(d->scale) || d->scale < 0.f)
+    return ra_fail(RA_ERR_INVALID, "scale must be finite and positive (0 = default)");
   s->B = d->batch;
   s->H = d->heads;
   s->Lq = d->q_len;

@@ -77,7 +77,7 @@ typedef struct ra_dims {
   int32_t kv_len;    /* Lk: tokens per key/value block */
   int32_t head_dim;  /* d */
   int32_t dtype;     /* RA_BF16 or RA_FP32: dtype of q, kv_block and dout */
-  float scale;       /* 0 => 1/sqrt(head_dim) */
+  float scale;       /* > 0; 0 => 1/sqrt(head_dim); negative is rejected */
 } ra_dims;
 
 /* Version of this ABI (major * 100 + minor). */

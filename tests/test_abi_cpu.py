@@ -81,6 +81,7 @@ def test_unsupported_and_invalid_dims(lib):
     assert _fwd(lib, _dims(batch=-1)) == -1
     assert _fwd(lib, _dims(q_len=64, kv_len=32)) == -1           # causal needs equal blocks
     assert _fwd(lib, _dims(scale=float("inf"))) == -1
+    assert _fwd(lib, _dims(scale=-0.5)) == -1
     # the backward is bf16-only
     d = _dims(dtype=1)
     assert lib.ring_attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, 1, 1, 64, 64, FAKE, FAKE,
