@@ -26,7 +26,7 @@ SOURCES = ["api.cpp", "emulator.cpp", "elementwise.hip", "fwd_fp32.hip",
 
 ARCH = "gfx950"
 # Packed fp32 VALU instructions are disabled on purpose for every HIP source.
-FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wno-inline-asm",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}"]
 

@@ -61,7 +61,6 @@ using namespace ra;
 
 namespace {
 
-typedef __attribute__((address_space(1))) void gvoid;
 typedef __attribute__((address_space(3))) void lvoid;
 
 constexpr float kRescaleThresh = 8.0f;  // log2 units
@@ -74,6 +73,20 @@ __device__ __forceinline__ int swz(int r) {
   else
     return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
+
+// Direct-to-LDS copy of 16 bytes per lane: lane l's bytes land at LDS byte
+// address lds_base + 16*l (lds_base wave-uniform).  Issued from inline asm so
+// that the compiler does not order every later LDS read after it; the kernel
+// waits for these loads itself (s_waitcnt vmcnt + barrier) before reading the
+// stage they fill.  The instruction has no register outputs.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_base) : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maxima).  The builtin,
+// unlike inline asm, tells the compiler that earlier global loads are done.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int D, int BN, int NW>
 struct FwdCfg {
@@ -99,6 +112,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
   constexpr int DS = D / 16;   // 16-wide head-dim slices (S contraction)
   constexpr int DD = D / 32;   // 32-wide head-dim tiles (O^T rows)
   __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGEB];
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(lvoid*)smem;  // LDS byte address
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hl = lane >> 5;
@@ -126,9 +140,30 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
   int ntw = 0;
   if (qw0 < Lq) ntw = diag ? min(ntiles, qw_last / BN + 1) : ntiles;
 
-  auto issue_tile = [&](int t) {
+  // Per-lane LDS byte offsets.  The swizzle of a row depends only on its low
+  // four bits, which do not change between 32-key sub-tiles, so one offset
+  // per head-dim slice serves every sub-tile (the sub-tile goes into the
+  // instruction's immediate offset).
+  int koff[DS];
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds)
+    koff[ds] = l32 * C::ROWB + (((2 * ds + hl) ^ swz<D>(l32)) << 4);
+  int voff[DD][2];
+  {
+    const int r = 4 * hl + ((lane & 15) >> 2);
+#pragma unroll
+    for (int dd = 0; dd < DD; ++dd) {
+      const int chunk = 4 * dd + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+        voff[dd][h2] = C::TILEB + (r + 8 * h2) * C::ROWB +
+                       ((chunk ^ swz<D>(r + 8 * h2)) << 4) + 8 * (lane & 1);
+    }
+  }
+
+  auto issue_tile = [&](int t) __attribute__((always_inline)) {
     const int kt0 = t * BN;
-    char* stage = smem + (t % C::NSTAGE) * C::STAGEB;
+    const uint32_t stage = smem_lds + (t % C::NSTAGE) * C::STAGEB;
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
       const int j = wave * C::LPW + i;
@@ -139,7 +174,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
       const int lc = ((q % C::ROWB) >> 4) ^ swz<D>(row);
       const int key = min(kt0 + row, Lk - 1);
       const bf16* src = (tensor ? Vp : Kp) + (size_t)key * D + lc * 8;
-      __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)(stage + j * 1024), 16, 0, 0);
+      dma16(src, __builtin_amdgcn_readfirstlane(stage + j * 1024));
     }
   };
 
@@ -156,46 +191,39 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
 #pragma unroll
   for (int dd = 0; dd < DD; ++dd) oacc[dd] = f32x16{};
   float m = kNegBig, lsum = 0.f;
-  f32x16 s[KK];    // scores of the tile being softmaxed
+  f32x16 s[KK];      // scores of the tile being softmaxed
   bf16x8 pb[KK][2];  // its probabilities, bf16, as PV B operands
 
   // Iteration 0 reads tiles 0 and 1.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  wait_vmem();
   __syncthreads();
 
-  auto scores = [&](int t) {  // s = K(t) Q^T
-    const char* ks = smem + (t % C::NSTAGE) * C::STAGEB;
+  auto scores = [&](const char* stage) __attribute__((always_inline)) {  // s = K Q^T
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) s[kk] = f32x16{};
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const int row = kk * 32 + l32;
-        const int pc = (2 * ds + hl) ^ swz<D>(row);
-        const bf16x8 a = *(const bf16x8*)(ks + row * C::ROWB + pc * 16);
+        const bf16x8 a = *(const bf16x8*)(stage + kk * 32 * C::ROWB + koff[ds]);
         s[kk] = mfma32(a, qreg[ds], s[kk]);
       }
   };
-  auto value = [&](int t) {  // O^T += V(t)^T P^T
-    const char* vs = smem + (t % C::NSTAGE) * C::STAGEB + C::TILEB;
+  auto value = [&](const char* stage) __attribute__((always_inline)) {  // O^T += V^T P^T
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int row = kk * 32 + 16 * half + 4 * hl + ((lane & 15) >> 2);
+        const char* vb = stage + (kk * 32 + 16 * half) * C::ROWB;
 #pragma unroll
         for (int dd = 0; dd < DD; ++dd) {
-          const int chunk = 4 * dd + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-          const int sub = 8 * (lane & 1);
-          const bf16x4 lo = lds_read_tr((const bf16*)(vs + row * C::ROWB + ((chunk ^ swz<D>(row)) << 4) + sub));
-          const bf16x4 hi = lds_read_tr((const bf16*)(vs + (row + 8) * C::ROWB +
-                                                      ((chunk ^ swz<D>(row + 8)) << 4) + sub));
+          const bf16x4 lo = lds_read_tr((const bf16*)(vb + voff[dd][0]));
+          const bf16x4 hi = lds_read_tr((const bf16*)(vb + voff[dd][1]));
           oacc[dd] = mfma32(cat(lo, hi), pb[kk][half], oacc[dd]);
         }
       }
   };
-  auto softmax = [&](int t) {  // s (raw scores of tile t) -> pb, m, lsum
+  auto softmax = [&](int t) __attribute__((always_inline)) {  // s (raw scores of tile t) -> pb, m, lsum
     const int kt0 = t * BN;
     if ((kt0 + BN > Lk) || (diag && kt0 + BN - 1 > qw0)) {
 #pragma unroll
@@ -238,9 +266,13 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
     }
   };
 
+  auto stage_of = [&](int t) __attribute__((always_inline)) -> const char* {
+    return smem + (t % C::NSTAGE) * C::STAGEB;
+  };
+
   // Group A computes the scores of tile 0 before the loop; group B computes
   // the scores of tile t inside iteration t.
-  if (!group_b && ntw > 0) scores(0);
+  if (!group_b && ntw > 0) scores(stage_of(0));
 
   for (int t = 0; t < ntiles; ++t) {
     if (t + 2 < ntiles) issue_tile(t + 2);
@@ -250,32 +282,32 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
         softmax(t);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(1);
-        value(t);
-        if (t + 1 < ntw) scores(t + 1);
+        value(stage_of(t));
+        if (t + 1 < ntw) scores(stage_of(t + 1));
         __builtin_amdgcn_s_setprio(0);
       }
     } else {
       // B: value(t-1) + scores(t), then softmax(t)
       if (t >= 1 && t - 1 < ntw) {
         __builtin_amdgcn_s_setprio(1);
-        value(t - 1);
-        if (t < ntw) scores(t);
+        value(stage_of(t - 1));
+        if (t < ntw) scores(stage_of(t));
         __builtin_amdgcn_s_setprio(0);
       } else if (t == 0 && ntw > 0) {
         __builtin_amdgcn_s_setprio(1);
-        scores(0);
+        scores(stage_of(0));
         __builtin_amdgcn_s_setprio(0);
       }
       __builtin_amdgcn_sched_barrier(0);
       if (t < ntw) softmax(t);
     }
     // Iteration t+1 reads tile t+2 (group A's scores), issued above.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vmem();
     __syncthreads();
   }
   // Group B still owes the value product of its last tile; no load touched
   // that stage after the loop.
-  if (group_b && ntw == ntiles && ntw > 0) value(ntw - 1);
+  if (group_b && ntw == ntiles && ntw > 0) value(stage_of(ntw - 1));
 
   // Fold the block partial into the running accumulators.
   const float ltot = add_halves(lsum);
