@@ -7,15 +7,19 @@
 // page, definition) and delta_i = <dO_i, O_i>:
 //     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - delta),
 //     dQ = scale * dS K,  dK = scale * dS^T Q.
-// Two kernels, no atomics, so every result is deterministic:
-//   * dq_kernel (query-major): a wave keeps 32 queries and their dO rows in
-//     registers, sweeps the key tiles of the block through LDS and
-//     accumulates dQ^T = K^T dS^T, reusing the forward's operand layout
-//     (S^T = K Q^T, dP^T = V dO^T; K^T from LDS transpose reads);
+// Two kernels and no atomics, so every result is deterministic:
+//   * dq_kernel (query-major, the forward's structure): a wave keeps 32
+//     queries and their dO rows in registers and sweeps the block's key /
+//     value tiles through LDS, forming S^T = K Q^T and dP^T = V dO^T (16-byte
+//     LDS reads), dS^T in registers, and dQ^T += K^T dS^T (K^T by LDS
+//     transpose reads).  Eight waves ping-pong as in the forward.
 //   * dkv_kernel (key-major): a wave keeps 32 keys and their values in
-//     registers, sweeps the query tiles (Q, dO, lse, delta) through LDS and
-//     accumulates dV = P^T dO and dK = dS^T Q, with dO^T and Q^T read
-//     transposed from LDS.
+//     registers and sweeps the query tiles (Q, dO, lse, delta) through LDS,
+//     forming S = Q K^T and dP = dO V^T, then dV += P^T dO and dK += dS^T Q
+//     with dO^T and Q^T by LDS transpose reads.  Four waves, one per SIMD;
+//     each wave overlaps the products of tile t with the scores of t+1.
+// Tiles move global -> LDS with direct-to-LDS copies into XOR-swizzled rows
+// (see ra_common.h), four stages deep, one tile of prefetch.
 // The causal diagonal block masks key j > query i; past blocks are dense.
 #include <math.h>
 
@@ -25,30 +29,61 @@ using namespace ra;
 
 namespace {
 
-constexpr int kNW = 4;  // waves per workgroup
+template <int D, int BT, int NW>
+struct TileCfg {
+  static constexpr int NT = NW * 64;
+  static constexpr int ROWB = D * 2;
+  static constexpr int TILEB = BT * ROWB;      // one [BT x D] bf16 tile
+  static constexpr int STAGEB = 2 * TILEB;     // two tiles per stage
+  static constexpr int NSTAGE = 4;
+  static constexpr int LPW = STAGEB / (NW * 1024);
+  static_assert(STAGEB % (NW * 1024) == 0 && LPW >= 1, "tile must split into 1 KiB loads");
+  static_assert(TILEB % 1024 == 0, "a load must not straddle the two tiles");
+};
+
+// Copy rows [t0, t0 + BT) of two [L x D] bf16 tensors into one stage;
+// rows past the end load the last valid row (masked by the caller).
+template <int D, int BT, int NW>
+__device__ __forceinline__ void issue_pair(uint32_t stage, const bf16* A, const bf16* B, int t0,
+                                           int L, int wave, int lane) {
+  using C = TileCfg<D, BT, NW>;
+#pragma unroll
+  for (int i = 0; i < C::LPW; ++i) {
+    const int j = wave * C::LPW + i;
+    const int p = j * 1024 + lane * 16;
+    const int which = p / C::TILEB;
+    const int q = p % C::TILEB;
+    const int row = q / C::ROWB;
+    const int lc = ((q % C::ROWB) >> 4) ^ swz<D>(row);
+    const int idx = min(t0 + row, L - 1);
+    const bf16* src = (which ? B : A) + (size_t)idx * D + lc * 8;
+    dma16(src, __builtin_amdgcn_readfirstlane(stage + j * 1024));
+  }
+}
 
 // ---------------------------------------------------------------- dQ ------
-template <int D, int BN>
-__global__ __launch_bounds__(kNW * 64, 1) void dq_kernel(
+template <int D, int BN, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ KV,
     const bf16* __restrict__ dO, const float* __restrict__ LSE,
     const float* __restrict__ Delta, float* __restrict__ dQacc, int BH, int Lq,
     int Lk, int n_qt, int diag, float c2, float scale) {
-  constexpr int BM = kNW * 32;
-  constexpr int LDW = D + 8;
-  constexpr int NT = kNW * 64;
-  constexpr int PT = BN * D / 8 / NT;
-  static_assert(BN * D / 8 % NT == 0, "tile split");
-  __shared__ __attribute__((aligned(16))) bf16 smem[2][2][BN * LDW];
+  using C = TileCfg<D, BN, NW>;
+  constexpr int BM = NW * 32;
+  constexpr int KK = BN / 32, DS = D / 16, DD = D / 32;
+  __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGEB];
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(lvoid*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hl = lane >> 5;
+  const bool group_b = NW == 8 && wave >= 4;
+  const int rblk = NW == 8 ? 2 * (wave & 3) + (wave >> 2) : wave;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / n_qt;
   int qt = tile % n_qt;
   if (diag) qt = n_qt - 1 - qt;
   const int q0 = qt * BM;
-  const int qw0 = q0 + wave * 32;
+  const int qw0 = q0 + rblk * 32;
   const int qi = qw0 + l32;
 
   const bf16* Qp = Q + (size_t)bh * Lq * D;
@@ -56,155 +91,167 @@ __global__ __launch_bounds__(kNW * 64, 1) void dq_kernel(
   const bf16* Kp = KV + (size_t)bh * Lk * D;
   const bf16* Vp = KV + ((size_t)BH + bh) * Lk * D;
 
-  bf16x8 qreg[D / 16], doreg[D / 16];
-#pragma unroll
-  for (int ds = 0; ds < D / 16; ++ds) {
-    if (qi < Lq) {
-      qreg[ds] = *(const bf16x8*)(Qp + (size_t)qi * D + ds * 16 + hl * 8);
-      doreg[ds] = *(const bf16x8*)(dOp + (size_t)qi * D + ds * 16 + hl * 8);
-    } else {
-      qreg[ds] = bf16x8{};
-      doreg[ds] = bf16x8{};
-    }
-  }
-  // Rows that saw no key (lse = -inf) cannot occur in a causal share, but
-  // keep them harmless: their probabilities are forced to zero.
-  const float lse_raw = qi < Lq ? LSE[(size_t)bh * Lq + qi] : -INFINITY;
-  const bool row_live = lse_raw != -INFINITY;
-  const float lse2 = row_live ? lse_raw * kLog2e : 0.f;
-  const float delta = qi < Lq ? Delta[(size_t)bh * Lq + qi] : 0.f;
-
-  f32x16 dq[D / 32];
-#pragma unroll
-  for (int dd = 0; dd < D / 32; ++dd) dq[dd] = f32x16{};
-
   const int kend = diag ? min(Lk, q0 + BM) : Lk;
   const int ntiles = (kend + BN - 1) / BN;
-  const int qw_last = min(qw0 + 32, Lq) - 1;
+  const int qw_last = min(qw0 + 31, Lq - 1);
+  int ntw = 0;
+  if (qw0 < Lq) ntw = diag ? min(ntiles, qw_last / BN + 1) : ntiles;
 
-  bf16x8 pk[PT], pv[PT];
-  auto gload = [&](int kt0) {
-#pragma unroll
-    for (int i = 0; i < PT; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int key = kt0 + row;
-      if (key < Lk) {
-        pk[i] = *(const bf16x8*)(Kp + (size_t)key * D + col);
-        pv[i] = *(const bf16x8*)(Vp + (size_t)key * D + col);
-      } else {
-        pk[i] = bf16x8{};
-        pv[i] = bf16x8{};
-      }
-    }
+  const LdsOffsets<D> off(lane);
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    issue_pair<D, BN, NW>(smem_lds + (t % C::NSTAGE) * C::STAGEB, Kp, Vp, t * BN, Lk, wave, lane);
   };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < PT; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *(bf16x8*)&smem[buf][0][row * LDW + col] = pk[i];
-      *(bf16x8*)&smem[buf][1][row * LDW + col] = pv[i];
-    }
-  };
+  if (ntiles > 0) issue(0);
+  if (ntiles > 1) issue(1);
 
-  if (ntiles > 0) {
-    gload(0);
-    sstore(0);
+  bf16x8 qreg[DS], doreg[DS];
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) {
+    qreg[ds] = qi < Lq ? *(const bf16x8*)(Qp + (size_t)qi * D + ds * 16 + hl * 8) : bf16x8{};
+    doreg[ds] = qi < Lq ? *(const bf16x8*)(dOp + (size_t)qi * D + ds * 16 + hl * 8) : bf16x8{};
   }
+  // A row that saw no key (lse = -inf) or lies past the end gets an
+  // exponent offset of +inf, so its probabilities are exactly zero.
+  const float lse_raw = qi < Lq ? LSE[(size_t)bh * Lq + qi] : -INFINITY;
+  const float neg_lse2 = lse_raw == -INFINITY ? -INFINITY : -lse_raw * kLog2e;
+  const float delta = qi < Lq ? Delta[(size_t)bh * Lq + qi] : 0.f;
+
+  f32x16 dq[DD];
+#pragma unroll
+  for (int dd = 0; dd < DD; ++dd) dq[dd] = f32x16{};
+  f32x16 s[KK], dp[KK];
+  bf16x8 pb[KK][2];
+
+  wait_vmem();
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const int kt0 = t * BN;
-    if (t + 1 < ntiles) gload(kt0 + BN);
-    const bool active = (qw0 < Lq) && (!diag || kt0 <= qw_last);
-    if (active) {
-      const bf16* Ks = smem[buf][0];
-      const bf16* Vs = smem[buf][1];
-      f32x16 s[BN / 32], dp[BN / 32];
+
+  auto stage_of = [&](int t) __attribute__((always_inline)) -> const char* {
+    return smem + (t % C::NSTAGE) * C::STAGEB;
+  };
+  auto scores = [&](const char* st) __attribute__((always_inline)) {  // S^T, dP^T
 #pragma unroll
-      for (int kk = 0; kk < BN / 32; ++kk) {
-        s[kk] = f32x16{};
-        dp[kk] = f32x16{};
+    for (int kk = 0; kk < KK; ++kk) {
+      s[kk] = f32x16{};
+      dp[kk] = f32x16{};
+    }
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const char* rb = st + kk * 32 * C::ROWB + off.row[ds];
+        s[kk] = mfma32(*(const bf16x8*)rb, qreg[ds], s[kk]);
+        dp[kk] = mfma32(*(const bf16x8*)(rb + C::TILEB), doreg[ds], dp[kk]);
       }
+  };
+  auto grad = [&](int t) __attribute__((always_inline)) {  // dS^T -> pb
+    const int kt0 = t * BN;
+    if ((kt0 + BN > Lk) || (diag && kt0 + BN - 1 > qw0)) {
 #pragma unroll
-      for (int ds = 0; ds < D / 16; ++ds)
-#pragma unroll
-        for (int kk = 0; kk < BN / 32; ++kk) {
-          const int off = (kk * 32 + l32) * LDW + ds * 16 + hl * 8;
-          s[kk] = mfma32(*(const bf16x8*)(Ks + off), qreg[ds], s[kk]);
-          dp[kk] = mfma32(*(const bf16x8*)(Vs + off), doreg[ds], dp[kk]);
-        }
-      const bool need_mask = (kt0 + BN > Lk) || (diag && kt0 + BN - 1 > qw0);
-#pragma unroll
-      for (int kk = 0; kk < BN / 32; ++kk)
+      for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = exp2_fast(s[kk][r] * c2 - lse2);
-          if (!row_live) p = 0.f;
-          if (need_mask) {
-            const int kj = kt0 + kk * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-            if (kj >= Lk || (diag && kj > qi)) p = 0.f;
-          }
-          s[kk][r] = p * (dp[kk][r] - delta);  // dS^T
-        }
-      // dQ^T += K^T dS^T (K^T operand by transpose reads, keys permuted to
-      // match the dS^T register layout).
-#pragma unroll
-      for (int kk = 0; kk < BN / 32; ++kk)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const bf16x8 b = to_bf16x8(s[kk], half);
-          const int rowA = kk * 32 + 16 * half + 4 * hl + ((lane & 15) >> 2);
-#pragma unroll
-          for (int dd = 0; dd < D / 32; ++dd) {
-            const int col = dd * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-            const bf16x8 a = cat(lds_read_tr(Ks + rowA * LDW + col),
-                                 lds_read_tr(Ks + (rowA + 8) * LDW + col));
-            dq[dd] = mfma32(a, b, dq[dd]);
-          }
+          const int kj = kt0 + kk * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (kj >= Lk || (diag && kj > qi)) s[kk][r] = -INFINITY;
         }
     }
-    if (t + 1 < ntiles) sstore(buf ^ 1);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2_fast(fmaf(s[kk][r], c2, neg_lse2));
+        s[kk][r] = p * (dp[kk][r] - delta);
+      }
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      pb[kk][0] = to_bf16x8(s[kk], 0);
+      pb[kk][1] = to_bf16x8(s[kk], 1);
+    }
+  };
+  auto value = [&](const char* st) __attribute__((always_inline)) {  // dQ^T += K^T dS^T
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const char* kb = st + (kk * 32 + 16 * half) * C::ROWB;
+#pragma unroll
+        for (int dd = 0; dd < DD; ++dd) {
+          const bf16x4 lo = lds_read_tr((const bf16*)(kb + off.tr[dd]));
+          const bf16x4 hi = lds_read_tr((const bf16*)(kb + off.tr[dd] + off.trd));
+          dq[dd] = mfma32(cat(lo, hi), pb[kk][half], dq[dd]);
+        }
+      }
+  };
+
+  if (!group_b && ntw > 0) scores(stage_of(0));
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 2 < ntiles) issue(t + 2);
+    if (!group_b) {
+      if (t < ntw) {
+        grad(t);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+        value(stage_of(t));
+        if (t + 1 < ntw) scores(stage_of(t + 1));
+        __builtin_amdgcn_s_setprio(0);
+      }
+    } else {
+      if (t >= 1 && t - 1 < ntw) {
+        __builtin_amdgcn_s_setprio(1);
+        value(stage_of(t - 1));
+        if (t < ntw) scores(stage_of(t));
+        __builtin_amdgcn_s_setprio(0);
+      } else if (t == 0 && ntw > 0) {
+        __builtin_amdgcn_s_setprio(1);
+        scores(stage_of(0));
+        __builtin_amdgcn_s_setprio(0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (t < ntw) grad(t);
+    }
+    wait_vmem();
     __syncthreads();
   }
+  if (group_b && ntw == ntiles && ntw > 0) value(stage_of(ntw - 1));
 
   if (qi < Lq) {
     float* row = dQacc + ((size_t)bh * Lq + qi) * D;
+    f32x4 old[DD][4];  // all loads first, then the stores
 #pragma unroll
-    for (int dd = 0; dd < D / 32; ++dd)
+    for (int dd = 0; dd < DD; ++dd)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) old[dd][g] = *(const f32x4*)(row + dd * 32 + 8 * g + 4 * hl);
+#pragma unroll
+    for (int dd = 0; dd < DD; ++dd)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d = dd * 32 + 8 * g + 4 * hl;
         const f32x4 v = {dq[dd][4 * g], dq[dd][4 * g + 1], dq[dd][4 * g + 2], dq[dd][4 * g + 3]};
-        *(f32x4*)(row + d) += v * scale;
+        *(f32x4*)(row + dd * 32 + 8 * g + 4 * hl) = old[dd][g] + v * scale;
       }
   }
 }
 
 // --------------------------------------------------------------- dK, dV ---
-template <int D, int BQ>
-__global__ __launch_bounds__(kNW * 64, 1) void dkv_kernel(
+template <int D, int BQ, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ KV,
     const bf16* __restrict__ dO, const float* __restrict__ LSE,
     const float* __restrict__ Delta, float* __restrict__ dKV, int BH, int Lq,
     int Lk, int n_kt, int diag, float c2, float scale) {
-  constexpr int BK = kNW * 32;  // keys per workgroup
-  constexpr int LDW = D + 8;
-  constexpr int NT = kNW * 64;
-  constexpr int PT = BQ * D / 8 / NT;
-  static_assert(BQ * D / 8 % NT == 0, "tile split");
-  static_assert(BQ <= NT, "one thread per row of lse / delta");
-  __shared__ __attribute__((aligned(16))) bf16 smem[2][2][BQ * LDW];
-  __shared__ float s_lse[2][BQ], s_delta[2][BQ];
+  using C = TileCfg<D, BQ, NW>;
+  constexpr int BK = NW * 32;  // keys per workgroup
+  constexpr int QS = BQ / 32, DS = D / 16, DD = D / 32;
+  static_assert(2 * BQ <= C::NT, "one thread per lse / delta value");
+  __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGEB];
+  __shared__ __attribute__((aligned(16))) float s_ld[C::NSTAGE][2][BQ];  // lse*log2e (neg), delta
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(lvoid*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hl = lane >> 5;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / n_kt;
-  const int k0 = (tile % n_kt) * BK;
+  const int k0 = (tile % n_kt) * BK;  // small k0 first: the most causal work
   const int kw0 = k0 + wave * 32;
-  const int kj = kw0 + l32;  // this lane's key (as the MFMA n index)
+  const int kj = kw0 + l32;
 
   const bf16* Qp = Q + (size_t)bh * Lq * D;
   const bf16* dOp = dO + (size_t)bh * Lq * D;
@@ -213,190 +260,220 @@ __global__ __launch_bounds__(kNW * 64, 1) void dkv_kernel(
   const float* Lp = LSE + (size_t)bh * Lq;
   const float* Dp = Delta + (size_t)bh * Lq;
 
-  bf16x8 kreg[D / 16], vreg[D / 16];
-#pragma unroll
-  for (int ds = 0; ds < D / 16; ++ds) {
-    if (kj < Lk) {
-      kreg[ds] = *(const bf16x8*)(Kp + (size_t)kj * D + ds * 16 + hl * 8);
-      vreg[ds] = *(const bf16x8*)(Vp + (size_t)kj * D + ds * 16 + hl * 8);
-    } else {
-      kreg[ds] = bf16x8{};
-      vreg[ds] = bf16x8{};
-    }
-  }
-  f32x16 dk[D / 32], dv[D / 32];
-#pragma unroll
-  for (int dd = 0; dd < D / 32; ++dd) {
-    dk[dd] = f32x16{};
-    dv[dd] = f32x16{};
-  }
-
   // Under the causal mask only queries at or after the first key matter.
   const int qstart = diag ? (k0 / BQ) * BQ : 0;
   const int ntiles = qstart < Lq ? (Lq - qstart + BQ - 1) / BQ : 0;
-  const int kw_last = min(kw0 + 32, Lk) - 1;
+  const int kw_last = min(kw0 + 31, Lk - 1);
+  // this wave's active tiles: a suffix [ft, ntiles) (query tiles that end
+  // before its first key contribute nothing)
+  int ft = 0;
+  if (diag) ft = max(0, (kw0 - qstart) / BQ);
+  if (kw0 >= Lk) ft = ntiles;
 
-  bf16x8 pq[PT], pd[PT];
-  float pl = 0.f, pdl = 0.f;
-  auto gload = [&](int qt0) {
-#pragma unroll
-    for (int i = 0; i < PT; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int q = qt0 + row;
-      if (q < Lq) {
-        pq[i] = *(const bf16x8*)(Qp + (size_t)q * D + col);
-        pd[i] = *(const bf16x8*)(dOp + (size_t)q * D + col);
-      } else {
-        pq[i] = bf16x8{};
-        pd[i] = bf16x8{};
-      }
-    }
-    if (tid < BQ) {
-      const int q = qt0 + tid;
-      const float l = q < Lq ? Lp[q] : -INFINITY;
-      pl = l;
-      pdl = q < Lq ? Dp[q] : 0.f;
+  const LdsOffsets<D> off(lane);
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    issue_pair<D, BQ, NW>(smem_lds + (t % C::NSTAGE) * C::STAGEB, Qp, dOp, qstart + t * BQ, Lq,
+                          wave, lane);
+  };
+  // lse / delta of a query tile: thread i < BQ loads lse, BQ <= i < 2BQ
+  // delta.  The raw value is held in a register while the loads of the
+  // iteration are in flight and converted only when stored to LDS.
+  float ld_reg = 0.f;
+  // (Threads < 2*BQ are whole waves, so the branches below do not diverge
+  // within a wave; the load itself is unconditional on a clamped row.)
+  auto load_ld = [&](int t) __attribute__((always_inline)) {
+    if (tid < 2 * BQ) {
+      const int q = min(qstart + t * BQ + (tid % BQ), Lq - 1);
+      ld_reg = (tid < BQ ? Lp : Dp)[q];
     }
   };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < PT; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *(bf16x8*)&smem[buf][0][row * LDW + col] = pq[i];
-      *(bf16x8*)&smem[buf][1][row * LDW + col] = pd[i];
-    }
-    if (tid < BQ) {
-      // -inf (an empty or out-of-range row) becomes +inf in the exponent
-      // offset, so that row's probabilities come out as exactly zero.
-      s_lse[buf][tid] = pl == -INFINITY ? INFINITY : pl * kLog2e;
-      s_delta[buf][tid] = pdl;
+  auto store_ld = [&](int t) __attribute__((always_inline)) {
+    if (tid < 2 * BQ) {
+      const bool valid = qstart + t * BQ + (tid % BQ) < Lq;
+      float v;
+      if (tid < BQ)  // negated lse in log2 units; -inf (dead or past the end): P = 0
+        v = (!valid || ld_reg == -INFINITY) ? -INFINITY : -ld_reg * kLog2e;
+      else
+        v = valid ? ld_reg : 0.f;
+      s_ld[t % C::NSTAGE][tid / BQ][tid % BQ] = v;
     }
   };
 
   if (ntiles > 0) {
-    gload(qstart);
-    sstore(0);
+    issue(0);
+    load_ld(0);
+    store_ld(0);
   }
+  if (ntiles > 1) {
+    issue(1);
+    load_ld(1);
+    store_ld(1);
+  }
+
+  bf16x8 kreg[DS], vreg[DS];
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) {
+    kreg[ds] = kj < Lk ? *(const bf16x8*)(Kp + (size_t)kj * D + ds * 16 + hl * 8) : bf16x8{};
+    vreg[ds] = kj < Lk ? *(const bf16x8*)(Vp + (size_t)kj * D + ds * 16 + hl * 8) : bf16x8{};
+  }
+  f32x16 dk[DD], dv[DD];
+#pragma unroll
+  for (int dd = 0; dd < DD; ++dd) {
+    dk[dd] = f32x16{};
+    dv[dd] = f32x16{};
+  }
+  f32x16 s[QS], dp[QS];
+  bf16x8 pbf[QS][2], dsbf[QS][2];
+
+  wait_vmem();
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const int qt0 = qstart + t * BQ;
-    if (t + 1 < ntiles) gload(qt0 + BQ);
-    // skip query tiles that end before this wave's first key
-    const bool active = (kw0 < Lk) && (!diag || qt0 + BQ - 1 >= kw0);
-    if (active) {
-      const bf16* Qs = smem[buf][0];
-      const bf16* dOs = smem[buf][1];
-      f32x16 s[BQ / 32], dp[BQ / 32];
+
+  auto stage_of = [&](int t) __attribute__((always_inline)) -> const char* {
+    return smem + (t % C::NSTAGE) * C::STAGEB;
+  };
+  auto scores = [&](const char* st) __attribute__((always_inline)) {  // S = Q K^T, dP = dO V^T
 #pragma unroll
-      for (int qs = 0; qs < BQ / 32; ++qs) {
-        s[qs] = f32x16{};
-        dp[qs] = f32x16{};
-      }
-      // S = Q K^T and dP = dO V^T: lane holds key l32 and 16 queries.
-#pragma unroll
-      for (int ds = 0; ds < D / 16; ++ds)
-#pragma unroll
-        for (int qs = 0; qs < BQ / 32; ++qs) {
-          const int off = (qs * 32 + l32) * LDW + ds * 16 + hl * 8;
-          s[qs] = mfma32(*(const bf16x8*)(Qs + off), kreg[ds], s[qs]);
-          dp[qs] = mfma32(*(const bf16x8*)(dOs + off), vreg[ds], dp[qs]);
-        }
-      const bool need_mask = (kw0 + 31 >= Lk) || (diag && kw_last > qt0);
-#pragma unroll
-      for (int qs = 0; qs < BQ / 32; ++qs)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ql = qs * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          float p = exp2_fast(s[qs][r] * c2 - s_lse[buf][ql]);
-          if (need_mask && (kj >= Lk || (diag && kj > qt0 + ql))) p = 0.f;
-          s[qs][r] = p;                                   // P
-          dp[qs][r] = p * (dp[qs][r] - s_delta[buf][ql]);  // dS
-        }
-      // dV += P^T dO and dK += dS^T Q; the B operands (dO, Q with queries
-      // permuted to match the register layout) come from transpose reads.
-#pragma unroll
-      for (int qs = 0; qs < BQ / 32; ++qs)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const bf16x8 ap = to_bf16x8(s[qs], half);
-          const bf16x8 ads = to_bf16x8(dp[qs], half);
-          const int rowB = qs * 32 + 16 * half + 4 * hl + ((lane & 15) >> 2);
-#pragma unroll
-          for (int dd = 0; dd < D / 32; ++dd) {
-            const int col = dd * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-            const bf16x8 bdo = cat(lds_read_tr(dOs + rowB * LDW + col),
-                                   lds_read_tr(dOs + (rowB + 8) * LDW + col));
-            const bf16x8 bq = cat(lds_read_tr(Qs + rowB * LDW + col),
-                                  lds_read_tr(Qs + (rowB + 8) * LDW + col));
-            dv[dd] = mfma32(ap, bdo, dv[dd]);
-            dk[dd] = mfma32(ads, bq, dk[dd]);
-          }
-        }
+    for (int qs = 0; qs < QS; ++qs) {
+      s[qs] = f32x16{};
+      dp[qs] = f32x16{};
     }
-    if (t + 1 < ntiles) sstore(buf ^ 1);
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) {
+        const char* rb = st + qs * 32 * C::ROWB + off.row[ds];
+        s[qs] = mfma32(*(const bf16x8*)rb, kreg[ds], s[qs]);
+        dp[qs] = mfma32(*(const bf16x8*)(rb + C::TILEB), vreg[ds], dp[qs]);
+      }
+  };
+  auto grad = [&](int t) __attribute__((always_inline)) {  // P, dS -> bf16 operands
+    const int qt0 = qstart + t * BQ;
+    const int st = t % C::NSTAGE;
+    const bool need_mask = (kw0 + 31 >= Lk) || (diag && kw_last > qt0);
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int ql = qs * 32 + 8 * g + 4 * hl;
+        const f32x4 nl = *(const f32x4*)&s_ld[st][0][ql];
+        const f32x4 dl = *(const f32x4*)&s_ld[st][1][ql];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float p = exp2_fast(fmaf(s[qs][r], c2, nl[e]));
+          if (need_mask && (kj >= Lk || (diag && kj > qt0 + ql + e))) p = 0.f;
+          s[qs][r] = p;
+          dp[qs][r] = p * (dp[qs][r] - dl[e]);
+        }
+      }
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        pbf[qs][half] = to_bf16x8(s[qs], half);
+        dsbf[qs][half] = to_bf16x8(dp[qs], half);
+      }
+  };
+  auto products = [&](const char* st) __attribute__((always_inline)) {  // dV, dK
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const char* qb = st + (qs * 32 + 16 * half) * C::ROWB;
+#pragma unroll
+        for (int dd = 0; dd < DD; ++dd) {
+          const bf16x8 bdo = cat(lds_read_tr((const bf16*)(qb + C::TILEB + off.tr[dd])),
+                                 lds_read_tr((const bf16*)(qb + C::TILEB + off.tr[dd] + off.trd)));
+          const bf16x8 bq = cat(lds_read_tr((const bf16*)(qb + off.tr[dd])),
+                                lds_read_tr((const bf16*)(qb + off.tr[dd] + off.trd)));
+          dv[dd] = mfma32(pbf[qs][half], bdo, dv[dd]);
+          dk[dd] = mfma32(dsbf[qs][half], bq, dk[dd]);
+        }
+      }
+  };
+
+  if (ft == 0 && ntiles > 0) scores(stage_of(0));
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 2 < ntiles) {
+      issue(t + 2);
+      load_ld(t + 2);
+    }
+    if (t >= ft) {
+      grad(t);
+      __builtin_amdgcn_sched_barrier(0);
+      products(stage_of(t));
+    }
+    if (t + 1 < ntiles && t + 1 >= ft) scores(stage_of(t + 1));
+    if (t + 2 < ntiles) store_ld(t + 2);
+    wait_vmem();
     __syncthreads();
   }
 
-  // dK/dV rows: lane holds head-dim column dd*32 + l32 of keys
+  // dK / dV rows: lane holds head-dim column dd*32 + l32 of keys
   // kw0 + 8*(r/4) + 4*hl + r%4.
   float* dKp = dKV + (size_t)bh * Lk * D;
   float* dVp = dKV + ((size_t)BH + bh) * Lk * D;
 #pragma unroll
-  for (int dd = 0; dd < D / 32; ++dd)
+  for (int dd = 0; dd < DD; ++dd) {
+    // all loads of this head-dim tile first, then the stores
+    float ok[16], ov[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kw0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+      const size_t o = (size_t)min(key, Lk - 1) * D + dd * 32 + l32;
+      ok[r] = dKp[o];
+      ov[r] = dVp[o];
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = kw0 + 8 * (r >> 2) + 4 * hl + (r & 3);
       if (key < Lk) {
-        const size_t off = (size_t)key * D + dd * 32 + l32;
-        dKp[off] += dk[dd][r] * scale;
-        dVp[off] += dv[dd][r];
+        const size_t o = (size_t)key * D + dd * 32 + l32;
+        dKp[o] = ok[r] + dk[dd][r] * scale;
+        dVp[o] = ov[r] + dv[dd][r];
       }
     }
-}
-
-template <int D>
-hipError_t launch_dq(const void* q, const void* kv, const void* dout, const float* lse,
-                     const float* delta, float* dq, const ra_launch& a) {
-  const int BH = a.B * a.H;
-  constexpr int BM = kNW * 32;
-  const int n_qt = (a.Lq + BM - 1) / BM;
-  if ((long long)n_qt * BH <= 0) return hipSuccess;
-  hipLaunchKernelGGL((dq_kernel<D, 64>), dim3(n_qt * BH), dim3(kNW * 64), 0, a.stream,
-                     (const bf16*)q, (const bf16*)kv, (const bf16*)dout, lse, delta, dq, BH,
-                     a.Lq, a.Lk, n_qt, a.diag, a.scale * kLog2e, a.scale);
-  return hipGetLastError();
-}
-
-template <int D>
-hipError_t launch_dkv(const void* q, const void* kv, const void* dout, const float* lse,
-                      const float* delta, float* dkv, const ra_launch& a) {
-  const int BH = a.B * a.H;
-  constexpr int BK = kNW * 32;
-  const int n_kt = (a.Lk + BK - 1) / BK;
-  if ((long long)n_kt * BH <= 0) return hipSuccess;
-  hipLaunchKernelGGL((dkv_kernel<D, 64>), dim3(n_kt * BH), dim3(kNW * 64), 0, a.stream,
-                     (const bf16*)q, (const bf16*)kv, (const bf16*)dout, lse, delta, dkv, BH,
-                     a.Lq, a.Lk, n_kt, a.diag, a.scale * kLog2e, a.scale);
-  return hipGetLastError();
+  }
 }
 
 }  // namespace
 
+// BN = 64 keys per dQ tile with eight waves (256 query rows per workgroup);
+// BQ = 64 queries per dK/dV tile with four waves (128 keys per workgroup).
 hipError_t ra_launch_bwd_dq(const void* q, const void* kv, const void* dout,
                             const float* lse, const float* delta, float* dq_acc,
                             const ra_launch& a) {
-  if (a.D == 128) return launch_dq<128>(q, kv, dout, lse, delta, dq_acc, a);
-  if (a.D == 64) return launch_dq<64>(q, kv, dout, lse, delta, dq_acc, a);
-  return hipErrorInvalidValue;
+  constexpr int NW = 8, BM = NW * 32;
+  const int BH = a.B * a.H;
+  const int n_qt = (a.Lq + BM - 1) / BM;
+  if ((long long)n_qt * BH <= 0) return hipSuccess;
+  const float c2 = a.scale * kLog2e;
+#define RA_DQ(DD)                                                                         \
+  hipLaunchKernelGGL((dq_kernel<DD, 64, NW>), dim3(n_qt * BH), dim3(NW * 64), 0, a.stream, \
+                     (const bf16*)q, (const bf16*)kv, (const bf16*)dout, lse, delta, dq_acc, \
+                     BH, a.Lq, a.Lk, n_qt, a.diag, c2, a.scale)
+  if (a.D == 128) RA_DQ(128);
+  else if (a.D == 64) RA_DQ(64);
+  else return hipErrorInvalidValue;
+#undef RA_DQ
+  return hipGetLastError();
 }
 
 hipError_t ra_launch_bwd_dkv(const void* q, const void* kv, const void* dout,
                              const float* lse, const float* delta, float* dkv,
                              const ra_launch& a) {
-  if (a.D == 128) return launch_dkv<128>(q, kv, dout, lse, delta, dkv, a);
-  if (a.D == 64) return launch_dkv<64>(q, kv, dout, lse, delta, dkv, a);
-  return hipErrorInvalidValue;
+  constexpr int NW = 4, BK = NW * 32;
+  const int BH = a.B * a.H;
+  const int n_kt = (a.Lk + BK - 1) / BK;
+  if ((long long)n_kt * BH <= 0) return hipSuccess;
+  const float c2 = a.scale * kLog2e;
+#define RA_DKV(DD)                                                                          \
+  hipLaunchKernelGGL((dkv_kernel<DD, 64, NW>), dim3(n_kt * BH), dim3(NW * 64), 0, a.stream, \
+                     (const bf16*)q, (const bf16*)kv, (const bf16*)dout, lse, delta, dkv, BH, \
+                     a.Lq, a.Lk, n_kt, a.diag, c2, a.scale)
+  if (a.D == 128) RA_DKV(128);
+  else if (a.D == 64) RA_DKV(64);
+  else return hipErrorInvalidValue;
+#undef RA_DKV
+  return hipGetLastError();
 }

@@ -61,32 +61,7 @@ using namespace ra;
 
 namespace {
 
-typedef __attribute__((address_space(3))) void lvoid;
-
 constexpr float kRescaleThresh = 8.0f;  // log2 units
-
-// Physical 16-byte chunk of logical chunk c in row r is c ^ swz(r).
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128)
-    return ((r & 3) << 2) | ((r >> 2) & 3);
-  else
-    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-}
-
-// Direct-to-LDS copy of 16 bytes per lane: lane l's bytes land at LDS byte
-// address lds_base + 16*l (lds_base wave-uniform).  Issued from inline asm so
-// that the compiler does not order every later LDS read after it; the kernel
-// waits for these loads itself (s_waitcnt vmcnt + barrier) before reading the
-// stage they fill.  The instruction has no register outputs.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds_base) : "memory", "m0");
-}
-
-// s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maxima).  The builtin,
-// unlike inline asm, tells the compiler that earlier global loads are done.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int D, int BN, int NW>
 struct FwdCfg {
@@ -140,26 +115,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
   int ntw = 0;
   if (qw0 < Lq) ntw = diag ? min(ntiles, qw_last / BN + 1) : ntiles;
 
-  // Per-lane LDS byte offsets.  The swizzle of a row depends only on its low
-  // four bits, which do not change between 32-key sub-tiles, so one offset
-  // per head-dim slice serves every sub-tile (the sub-tile goes into the
-  // instruction's immediate offset).
-  int koff[DS];
-#pragma unroll
-  for (int ds = 0; ds < DS; ++ds)
-    koff[ds] = l32 * C::ROWB + (((2 * ds + hl) ^ swz<D>(l32)) << 4);
-  int voff[DD][2];
-  {
-    const int r = 4 * hl + ((lane & 15) >> 2);
-#pragma unroll
-    for (int dd = 0; dd < DD; ++dd) {
-      const int chunk = 4 * dd + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-        voff[dd][h2] = C::TILEB + (r + 8 * h2) * C::ROWB +
-                       ((chunk ^ swz<D>(r + 8 * h2)) << 4) + 8 * (lane & 1);
-    }
-  }
+  const LdsOffsets<D> off(lane);
 
   auto issue_tile = [&](int t) __attribute__((always_inline)) {
     const int kt0 = t * BN;
@@ -205,7 +161,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
     for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const bf16x8 a = *(const bf16x8*)(stage + kk * 32 * C::ROWB + koff[ds]);
+        const bf16x8 a = *(const bf16x8*)(stage + kk * 32 * C::ROWB + off.row[ds]);
         s[kk] = mfma32(a, qreg[ds], s[kk]);
       }
   };
@@ -214,11 +170,11 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
     for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const char* vb = stage + (kk * 32 + 16 * half) * C::ROWB;
+        const char* vb = stage + C::TILEB + (kk * 32 + 16 * half) * C::ROWB;
 #pragma unroll
         for (int dd = 0; dd < DD; ++dd) {
-          const bf16x4 lo = lds_read_tr((const bf16*)(vb + voff[dd][0]));
-          const bf16x4 hi = lds_read_tr((const bf16*)(vb + voff[dd][1]));
+          const bf16x4 lo = lds_read_tr((const bf16*)(vb + off.tr[dd]));
+          const bf16x4 hi = lds_read_tr((const bf16*)(vb + off.tr[dd] + off.trd));
           oacc[dd] = mfma32(cat(lo, hi), pb[kk][half], oacc[dd]);
         }
       }
@@ -330,16 +286,19 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
       wb = eb / z * inv;
     }
     float* orow = Oacc + ((size_t)bh * Lq + qi) * D;
+    f32x4 oa[DD][4];  // all loads first, then the stores
+#pragma unroll
+    for (int dd = 0; dd < DD; ++dd)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        oa[dd][g] = wa != 0.f ? *(const f32x4*)(orow + dd * 32 + 8 * g + 4 * hl) : f32x4{};
 #pragma unroll
     for (int dd = 0; dd < DD; ++dd)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d = dd * 32 + 8 * g + 4 * hl;
         const f32x4 acc = {oacc[dd][4 * g], oacc[dd][4 * g + 1], oacc[dd][4 * g + 2],
                            oacc[dd][4 * g + 3]};
-        f32x4 res = acc * wb;
-        if (wa != 0.f) res += *(const f32x4*)(orow + d) * wa;
-        *(f32x4*)(orow + d) = res;
+        *(f32x4*)(orow + dd * 32 + 8 * g + 4 * hl) = acc * wb + oa[dd][g] * wa;
       }
     if (hl == 0) *lse_p = lse_new;
   }

@@ -72,6 +72,62 @@ __device__ __forceinline__ int xcd_remap(int w, int n) {
   return (w & 7) * (n >> 3) + (w >> 3);
 }
 
+// ---- tile staging: swizzled LDS rows filled by direct-to-LDS copies ------
+
+typedef __attribute__((address_space(3))) void lvoid;
+
+// Physical 16-byte chunk of logical chunk c in row r is c ^ swz(r).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128)
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  else
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Direct-to-LDS copy of 16 bytes per lane: lane l's bytes land at LDS byte
+// address lds_base + 16*l (lds_base wave-uniform).  Issued from inline asm so
+// that the compiler does not order every later LDS read after it; the kernel
+// waits for these loads itself (s_waitcnt vmcnt + barrier) before reading the
+// stage they fill.  The instruction has no register outputs.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_base) : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maxima).  The builtin,
+// unlike inline asm, tells the compiler that earlier global loads are done.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Per-lane byte offsets inside a swizzled [rows x D] bf16 tile:
+//   row[ds]  16-byte read of row 32*k + l32, chunk 2*ds + hl (MFMA A/B rows);
+//   tr[dd]   transpose read of the 4x16 block at rows 16*k + 4*hl + (lane%16)/4,
+//            columns 32*dd + 16*((lane/16)%2) + 4*(lane%4);
+//   trd      added to tr[dd] for the same block 8 rows further down.
+// None depends on k (the swizzle only uses the low four row bits), so k goes
+// into the instruction's immediate offset.  The +8-row partner differs by a
+// lane constant: row 8 flips bit 1 of the swizzle, which moves the chunk by
+// +-2 depending on bit 1 of (chunk ^ swizzle), a bit that no 32-column tile
+// index dd touches.
+template <int D>
+struct LdsOffsets {
+  int row[D / 16];
+  int tr[D / 32];
+  int trd;
+  __device__ __forceinline__ explicit LdsOffsets(int lane) {
+    constexpr int ROWB = D * 2;
+    const int l32 = lane & 31, hl = lane >> 5;
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) row[ds] = l32 * ROWB + (((2 * ds + hl) ^ swz<D>(l32)) << 4);
+    const int r = 4 * hl + ((lane & 15) >> 2);
+    const int c = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int dd = 0; dd < D / 32; ++dd)
+      tr[dd] = r * ROWB + (((4 * dd + c) ^ swz<D>(r)) << 4) + 8 * (lane & 1);
+    trd = 8 * ROWB + ((((c ^ swz<D>(r)) >> 1) & 1) ? -32 : 32);
+  }
+};
+
 }  // namespace ra
 
 // ---- launchers (host side, defined in the .hip sources) --------------------
