@@ -41,26 +41,6 @@ struct TileCfg {
   static_assert(TILEB % 1024 == 0, "a load must not straddle the two tiles");
 };
 
-// Copy rows [t0, t0 + BT) of two [L x D] bf16 tensors into one stage;
-// rows past the end load the last valid row (masked by the caller).
-template <int D, int BT, int NW>
-__device__ __forceinline__ void issue_pair(uint32_t stage, const bf16* A, const bf16* B, int t0,
-                                           int L, int wave, int lane) {
-  using C = TileCfg<D, BT, NW>;
-#pragma unroll
-  for (int i = 0; i < C::LPW; ++i) {
-    const int j = wave * C::LPW + i;
-    const int p = j * 1024 + lane * 16;
-    const int which = p / C::TILEB;
-    const int q = p % C::TILEB;
-    const int row = q / C::ROWB;
-    const int lc = ((q % C::ROWB) >> 4) ^ swz<D>(row);
-    const int idx = min(t0 + row, L - 1);
-    const bf16* src = (which ? B : A) + (size_t)idx * D + lc * 8;
-    dma16(src, __builtin_amdgcn_readfirstlane(stage + j * 1024));
-  }
-}
-
 // ---------------------------------------------------------------- dQ ------
 template <int D, int BN, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
@@ -98,8 +78,9 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
   if (qw0 < Lq) ntw = diag ? min(ntiles, qw_last / BN + 1) : ntiles;
 
   const LdsOffsets<D> off(lane);
+  const StageLoader<D, BN, NW> loader(wave, lane);
   auto issue = [&](int t) __attribute__((always_inline)) {
-    issue_pair<D, BN, NW>(smem_lds + (t % C::NSTAGE) * C::STAGEB, Kp, Vp, t * BN, Lk, wave, lane);
+    loader.issue(smem_lds + (t % C::NSTAGE) * C::STAGEB, Kp, Vp, t * BN, Lk);
   };
   if (ntiles > 0) issue(0);
   if (ntiles > 1) issue(1);
@@ -145,7 +126,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
   };
   auto grad = [&](int t) __attribute__((always_inline)) {  // dS^T -> pb
     const int kt0 = t * BN;
-    if ((kt0 + BN > Lk) || (diag && kt0 + BN - 1 > qw0)) {
+    if (__builtin_amdgcn_readfirstlane((kt0 + BN > Lk) || (diag && kt0 + BN - 1 > qw0))) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
@@ -239,10 +220,11 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
     int Lk, int n_kt, int diag, float c2, float scale) {
   using C = TileCfg<D, BQ, NW>;
   constexpr int BK = NW * 32;  // keys per workgroup
-  constexpr int QS = BQ / 32, DS = D / 16, DD = D / 32;
+  constexpr int DS = D / 16, DD = D / 32;
+  static_assert(BQ == 64, "two 32-query sub-tiles per LDS tile");
   static_assert(2 * BQ <= C::NT, "one thread per lse / delta value");
   __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGEB];
-  __shared__ __attribute__((aligned(16))) float s_ld[C::NSTAGE][2][BQ];  // lse*log2e (neg), delta
+  __shared__ __attribute__((aligned(16))) float s_ld[C::NSTAGE][2][BQ];  // -lse*log2e, delta
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lvoid*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -264,23 +246,20 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
   const int qstart = diag ? (k0 / BQ) * BQ : 0;
   const int ntiles = qstart < Lq ? (Lq - qstart + BQ - 1) / BQ : 0;
   const int kw_last = min(kw0 + 31, Lk - 1);
-  // this wave's active tiles: a suffix [ft, ntiles) (query tiles that end
-  // before its first key contribute nothing)
-  int ft = 0;
-  if (diag) ft = max(0, (kw0 - qstart) / BQ);
+  // This wave's active tiles are a suffix [ft, ntiles): query tiles that
+  // end before its first key contribute nothing.
+  int ft = diag ? max(0, (kw0 - qstart) / BQ) : 0;
   if (kw0 >= Lk) ft = ntiles;
 
   const LdsOffsets<D> off(lane);
+  const StageLoader<D, BQ, NW> loader(wave, lane);
   auto issue = [&](int t) __attribute__((always_inline)) {
-    issue_pair<D, BQ, NW>(smem_lds + (t % C::NSTAGE) * C::STAGEB, Qp, dOp, qstart + t * BQ, Lq,
-                          wave, lane);
+    loader.issue(smem_lds + (t % C::NSTAGE) * C::STAGEB, Qp, dOp, qstart + t * BQ, Lq);
   };
   // lse / delta of a query tile: thread i < BQ loads lse, BQ <= i < 2BQ
-  // delta.  The raw value is held in a register while the loads of the
-  // iteration are in flight and converted only when stored to LDS.
+  // delta (whole waves, so no divergence); the raw value waits in a register
+  // while the iteration's loads are in flight and is converted on the store.
   float ld_reg = 0.f;
-  // (Threads < 2*BQ are whole waves, so the branches below do not diverge
-  // within a wave; the load itself is unconditional on a clamped row.)
   auto load_ld = [&](int t) __attribute__((always_inline)) {
     if (tid < 2 * BQ) {
       const int q = min(qstart + t * BQ + (tid % BQ), Lq - 1);
@@ -322,8 +301,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
     dk[dd] = f32x16{};
     dv[dd] = f32x16{};
   }
-  f32x16 s[QS], dp[QS];
-  bf16x8 pbf[QS][2], dsbf[QS][2];
+  // Work runs in 32-query sub-tiles (qs = 0, 1) of the 64-query LDS tiles.
+  f32x16 s, dp;            // S and dP of the sub-tile to be softmaxed next
+  bf16x8 pbf[2], dsbf[2];  // P and dS of the sub-tile being multiplied
+  bf16x8 ob[2][8];         // LDS operands, one MFMA step ahead
 
   wait_vmem();
   __syncthreads();
@@ -331,82 +312,137 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
   auto stage_of = [&](int t) __attribute__((always_inline)) -> const char* {
     return smem + (t % C::NSTAGE) * C::STAGEB;
   };
-  auto scores = [&](const char* st) __attribute__((always_inline)) {  // S = Q K^T, dP = dO V^T
+  // P = exp(S*scale - lse), dS = P (dP - delta) for sub-tile qs of tile t.
+  auto grad = [&](int t, int qs) __attribute__((always_inline)) {
+    const int qt0 = qstart + t * BQ + qs * 32;
+    const int st = t % C::NSTAGE;
+    f32x4 nl[4], dl[4];
 #pragma unroll
-    for (int qs = 0; qs < QS; ++qs) {
-      s[qs] = f32x16{};
-      dp[qs] = f32x16{};
+    for (int g = 0; g < 4; ++g) {
+      nl[g] = *(const f32x4*)&s_ld[st][0][qs * 32 + 8 * g + 4 * hl];
+      dl[g] = *(const f32x4*)&s_ld[st][1][qs * 32 + 8 * g + 4 * hl];
     }
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds)
+    for (int r = 0; r < 16; ++r) s[r] = exp2_fast(fmaf(s[r], c2, nl[r >> 2][r & 3]));
+    if (__builtin_amdgcn_readfirstlane((kw0 + 31 >= Lk) || (diag && kw_last > qt0))) {
 #pragma unroll
-      for (int qs = 0; qs < QS; ++qs) {
-        const char* rb = st + qs * 32 * C::ROWB + off.row[ds];
-        s[qs] = mfma32(*(const bf16x8*)rb, kreg[ds], s[qs]);
-        dp[qs] = mfma32(*(const bf16x8*)(rb + C::TILEB), vreg[ds], dp[qs]);
+      for (int r = 0; r < 16; ++r) {
+        const int q = qt0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        if (kj >= Lk || (diag && kj > q)) s[r] = 0.f;
       }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] - dl[r >> 2][r & 3]);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      pbf[half] = to_bf16x8(s, half);
+      dsbf[half] = to_bf16x8(dp, half);
+    }
   };
-  auto grad = [&](int t) __attribute__((always_inline)) {  // P, dS -> bf16 operands
-    const int qt0 = qstart + t * BQ;
-    const int st = t % C::NSTAGE;
-    const bool need_mask = (kw0 + 31 >= Lk) || (diag && kw_last > qt0);
+  // MFMA steps of 8.  Product steps p = 0, 1 (rows 16*p of the sub-tile):
+  // dV += P^T dO and dK += dS^T Q over the head-dim tiles, operands by
+  // transpose reads.  Score steps p = 2, 3 (head-dim slices (p-2)*DS/2 ..):
+  // S = Q K^T and dP = dO V^T, operands by 16-byte row reads; step 2 starts
+  // the accumulators from zero.
+  auto load_step = [&](int p, const char* st, int qs, bf16x8* o) __attribute__((always_inline)) {
+    if (p < 2) {
+      const char* qb = st + (qs * 32 + 16 * p) * C::ROWB;
 #pragma unroll
-    for (int qs = 0; qs < QS; ++qs)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int ql = qs * 32 + 8 * g + 4 * hl;
-        const f32x4 nl = *(const f32x4*)&s_ld[st][0][ql];
-        const f32x4 dl = *(const f32x4*)&s_ld[st][1][ql];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float p = exp2_fast(fmaf(s[qs][r], c2, nl[e]));
-          if (need_mask && (kj >= Lk || (diag && kj > qt0 + ql + e))) p = 0.f;
-          s[qs][r] = p;
-          dp[qs][r] = p * (dp[qs][r] - dl[e]);
-        }
+      for (int dd = 0; dd < DD; ++dd) {
+        o[2 * dd] = cat(lds_read_tr((const bf16*)(qb + C::TILEB + off.tr[dd])),
+                        lds_read_tr((const bf16*)(qb + C::TILEB + off.tr[dd] + off.trd)));
+        o[2 * dd + 1] = cat(lds_read_tr((const bf16*)(qb + off.tr[dd])),
+                            lds_read_tr((const bf16*)(qb + off.tr[dd] + off.trd)));
       }
+    } else {
 #pragma unroll
-    for (int qs = 0; qs < QS; ++qs)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        pbf[qs][half] = to_bf16x8(s[qs], half);
-        dsbf[qs][half] = to_bf16x8(dp[qs], half);
+      for (int j = 0; j < DS / 2; ++j) {
+        const char* rb = st + qs * 32 * C::ROWB + off.row[(DS / 2) * (p - 2) + j];
+        o[2 * j] = *(const bf16x8*)rb;
+        o[2 * j + 1] = *(const bf16x8*)(rb + C::TILEB);
       }
+    }
   };
-  auto products = [&](const char* st) __attribute__((always_inline)) {  // dV, dK
+  auto mfma_step = [&](int p, const bf16x8* o) __attribute__((always_inline)) {
+    if (p < 2) {
 #pragma unroll
-    for (int qs = 0; qs < QS; ++qs)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const char* qb = st + (qs * 32 + 16 * half) * C::ROWB;
-#pragma unroll
-        for (int dd = 0; dd < DD; ++dd) {
-          const bf16x8 bdo = cat(lds_read_tr((const bf16*)(qb + C::TILEB + off.tr[dd])),
-                                 lds_read_tr((const bf16*)(qb + C::TILEB + off.tr[dd] + off.trd)));
-          const bf16x8 bq = cat(lds_read_tr((const bf16*)(qb + off.tr[dd])),
-                                lds_read_tr((const bf16*)(qb + off.tr[dd] + off.trd)));
-          dv[dd] = mfma32(pbf[qs][half], bdo, dv[dd]);
-          dk[dd] = mfma32(dsbf[qs][half], bq, dk[dd]);
-        }
+      for (int dd = 0; dd < DD; ++dd) {
+        dv[dd] = mfma32(pbf[p], o[2 * dd], dv[dd]);
+        dk[dd] = mfma32(dsbf[p], o[2 * dd + 1], dk[dd]);
       }
+    } else {
+#pragma unroll
+      for (int j = 0; j < DS / 2; ++j) {
+        const int ds = (DS / 2) * (p - 2) + j;
+        const bool first = ds == 0;
+        s = mfma32(o[2 * j], kreg[ds], first ? f32x16{} : s);
+        dp = mfma32(o[2 * j + 1], vreg[ds], first ? f32x16{} : dp);
+      }
+    }
   };
-
-  if (ft == 0 && ntiles > 0) scores(stage_of(0));
-  for (int t = 0; t < ntiles; ++t) {
+  // Runs steps [p0, p1); the operands of step p0 must already be in ob[p0&1].
+  auto steps = [&](int p0, int p1, const char* pst, int pqs, const char* sst, int sqs)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      if (p >= p0 && p < p1) {
+        if (p + 1 < p1) load_step(p + 1, p + 1 < 2 ? pst : sst, p + 1 < 2 ? pqs : sqs, ob[(p + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);  // keep the next step's reads ahead
+        mfma_step(p, ob[p & 1]);
+      }
+    }
+  };
+  // Multiply sub-tile (t, qs), then score the next sub-tile (tn, 1 - qs).
+  auto full_phase = [&](int t, int qs, int tn) __attribute__((always_inline)) {
+    grad(t, qs);
+    __builtin_amdgcn_sched_barrier(0);
+    load_step(0, stage_of(t), qs, ob[0]);
+    steps(0, 4, stage_of(t), qs, stage_of(tn), 1 - qs);
+  };
+  auto score_phase = [&](int tn, int sqs) __attribute__((always_inline)) {
+    load_step(2, stage_of(tn), sqs, ob[0]);
+    steps(2, 4, nullptr, 0, stage_of(tn), sqs);
+  };
+  auto prod_phase = [&](int t, int qs) __attribute__((always_inline)) {
+    grad(t, qs);
+    __builtin_amdgcn_sched_barrier(0);
+    load_step(0, stage_of(t), qs, ob[0]);
+    steps(0, 2, stage_of(t), qs, nullptr, 0);
+  };
+  auto end_tile = [&](int t) __attribute__((always_inline)) {
+    if (t + 2 < ntiles) store_ld(t + 2);
+    wait_vmem();
+    __syncthreads();
+  };
+  auto begin_tile = [&](int t) __attribute__((always_inline)) {
     if (t + 2 < ntiles) {
       issue(t + 2);
       load_ld(t + 2);
     }
-    if (t >= ft) {
-      grad(t);
-      __builtin_amdgcn_sched_barrier(0);
-      products(stage_of(t));
-    }
-    if (t + 1 < ntiles && t + 1 >= ft) scores(stage_of(t + 1));
-    if (t + 2 < ntiles) store_ld(t + 2);
-    wait_vmem();
-    __syncthreads();
+  };
+
+  // Tiles before this wave's first active tile: only keep the pipeline
+  // moving; the last of them scores sub-tile (ft, 0).
+  int t = 0;
+  for (; t < min(ft, ntiles); ++t) {
+    begin_tile(t);
+    if (t + 1 == ft && ft < ntiles) score_phase(ft, 0);
+    end_tile(t);
+  }
+  if (ft == 0 && ntiles > 0) score_phase(0, 0);
+  // Steady state: both sub-tiles multiplied, the next two scored.
+  for (; t + 1 < ntiles; ++t) {
+    begin_tile(t);
+    full_phase(t, 0, t);
+    full_phase(t, 1, t + 1);
+    end_tile(t);
+  }
+  // Last tile: nothing left to score after its second sub-tile.
+  if (t < ntiles) {
+    begin_tile(t);
+    full_phase(t, 0, t);
+    prod_phase(t, 1);
+    end_tile(t);
   }
 
   // dK / dV rows: lane holds head-dim column dd*32 + l32 of keys

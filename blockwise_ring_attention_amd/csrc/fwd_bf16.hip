@@ -117,21 +117,9 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
 
   const LdsOffsets<D> off(lane);
 
+  const StageLoader<D, BN, NW> loader(wave, lane);
   auto issue_tile = [&](int t) __attribute__((always_inline)) {
-    const int kt0 = t * BN;
-    const uint32_t stage = smem_lds + (t % C::NSTAGE) * C::STAGEB;
-#pragma unroll
-    for (int i = 0; i < C::LPW; ++i) {
-      const int j = wave * C::LPW + i;
-      const int p = j * 1024 + lane * 16;
-      const int tensor = p / C::TILEB;
-      const int q = p % C::TILEB;
-      const int row = q / C::ROWB;
-      const int lc = ((q % C::ROWB) >> 4) ^ swz<D>(row);
-      const int key = min(kt0 + row, Lk - 1);
-      const bf16* src = (tensor ? Vp : Kp) + (size_t)key * D + lc * 8;
-      dma16(src, __builtin_amdgcn_readfirstlane(stage + j * 1024));
-    }
+    loader.issue(smem_lds + (t % C::NSTAGE) * C::STAGEB, Kp, Vp, t * BN, Lk);
   };
 
   if (ntiles > 0) issue_tile(0);
@@ -181,7 +169,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
   };
   auto softmax = [&](int t) __attribute__((always_inline)) {  // s (raw scores of tile t) -> pb, m, lsum
     const int kt0 = t * BN;
-    if ((kt0 + BN > Lk) || (diag && kt0 + BN - 1 > qw0)) {
+    // (wave-uniform; made scalar so the mask is a skipped branch, not selects)
+    if (__builtin_amdgcn_readfirstlane((kt0 + BN > Lk) || (diag && kt0 + BN - 1 > qw0))) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
 #pragma unroll

@@ -95,6 +95,56 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
                :: "v"(src), "s"(lds_base) : "memory", "m0");
 }
 
+// A pointer the caller knows to be wave-uniform, moved to scalar registers.
+template <typename T>
+__device__ __forceinline__ T* uniform(T* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Same copy with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// byte offset (the global_load saddr form): no per-lane address arithmetic.
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_base) : "memory", "m0");
+}
+
+// Copies one pipeline stage: two [BT x D] bf16 tiles (rows t0 .. t0+BT-1 of
+// tensors A and B, each [L x D]) into swizzled LDS rows, 1 KiB per wave
+// instruction.  Per-lane source offsets are fixed at construction; a tile
+// that runs past row L-1 takes a slower path that clamps rows to L-1 (the
+// caller masks them).
+template <int D, int BT, int NW>
+struct StageLoader {
+  static constexpr int ROWB = D * 2;
+  static constexpr int TILEB = BT * ROWB;
+  static constexpr int STAGEB = 2 * TILEB;
+  static constexpr int LPW = STAGEB / (NW * 1024);
+  static_assert(STAGEB % (NW * 1024) == 0 && LPW >= 1, "tile must split into 1 KiB loads");
+  static_assert(TILEB % 1024 == 0, "a load must not straddle the two tiles");
+  int wave, lane;  // wave must be wave-uniform
+  __device__ __forceinline__ StageLoader(int wave_, int lane_) : wave(wave_), lane(lane_) {}
+  __device__ __forceinline__ void issue(uint32_t stage_lds, const bf16* A, const bf16* B, int t0,
+                                        int L) const {
+    const bool full = t0 + BT <= L;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int j = wave * LPW + i;
+      const int q = (j * 1024 + lane * 16) % TILEB;
+      const int row = q / ROWB;
+      const int lc = ((q % ROWB) >> 4) ^ swz<D>(row);
+      const bf16* base = (j * 1024) / TILEB ? B : A;
+      const uint32_t lds = __builtin_amdgcn_readfirstlane(stage_lds + j * 1024);
+      if (full)
+        dma16_s(uniform(base + (size_t)t0 * D), (uint32_t)(row * ROWB + lc * 16), lds);
+      else
+        dma16(base + (size_t)min(t0 + row, L - 1) * D + lc * 8, lds);
+    }
+  }
+};
+
 // s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maxima).  The builtin,
 // unlike inline asm, tells the compiler that earlier global loads are done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
