@@ -49,7 +49,53 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phases", action="store_true",
                     help="skip the separate forward-only / backward-only timings")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (a known amount of "
+                         "HBM traffic, to scale the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+def _copy_calibration():
+    """One torch copy kernel over 1 GiB: reads 1 GiB, writes 1 GiB."""
+    import torch
+    n = 1 << 28  # float32 elements = 1 GiB
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4}), flush=True)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_lwm7b_fwd_bwd.json")
+KERNEL_SOURCES = {
+    "fwd_bf16": ["blockwise_ring_attention_amd/csrc/fwd_bf16.hip"],
+    "bwd_dq": ["blockwise_ring_attention_amd/csrc/bwd_bf16.hip"],
+    "bwd_dkv": ["blockwise_ring_attention_amd/csrc/bwd_bf16.hip"],
+}
+COMMON_SOURCE = "blockwise_ring_attention_amd/csrc/ra_common.h"
+
+
+def _measured_traffic(family):
+    """HBM bytes per launch of a kernel family from the committed FETCH_SIZE /
+    WRITE_SIZE counter runs (scaled by the copy calibration), or None when the
+    kernel's source has changed since the counters were taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        k = rec["kernels"][family]
+        h = hashlib.sha256()
+        for path in KERNEL_SOURCES[family] + [COMMON_SOURCE]:
+            with open(os.path.join(ROOT, path), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest()[:16] != k["source_sha256_16"]:
+            return None
+        kib = k["fetch_kib_per_dispatch"] * rec["fetch_factor"] + \
+            k["write_kib_per_dispatch"] * rec["write_factor"]
+        return int(kib * 1024)
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def _cpu_baseline(host, cfg, rank, target_s):
@@ -106,6 +152,10 @@ def main():
               f"(WORLD_SIZE {world}) is not supported: the multi-GPU ring is not part of this "
               "build.", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        _copy_calibration()
+        return
 
     import torch
 
@@ -188,7 +238,8 @@ def main():
                            "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
     dom = max(per_kernel, key=lambda f: per_kernel[f]["total_ms_per_step"])
     roofline = {"bound": "mfma", "achieved": per_kernel[dom]["tflops"], "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": per_kernel[dom]["frac"], "traffic": None,
+                "unit": "TFLOP/s", "frac": per_kernel[dom]["frac"],
+                "traffic": _measured_traffic(dom), "traffic_unit": "HBM bytes per launch",
                 "kernel": dom}
 
     result = {

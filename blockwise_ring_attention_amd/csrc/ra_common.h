@@ -129,10 +129,15 @@ struct StageLoader {
   __device__ __forceinline__ void issue(uint32_t stage_lds, const bf16* A, const bf16* B, int t0,
                                         int L) const {
     const bool full = t0 + BT <= L;
+    // Recompute the per-lane offsets at each call instead of letting them be
+    // hoisted into registers that live across the whole loop (they are a
+    // few integer operations; held registers have been spilled).
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int j = wave * LPW + i;
-      const int q = (j * 1024 + lane * 16) % TILEB;
+      const int q = (j * 1024 + ln * 16) % TILEB;
       const int row = q / ROWB;
       const int lc = ((q % ROWB) >> 4) ^ swz<D>(row);
       const bf16* base = (j * 1024) / TILEB ? B : A;
