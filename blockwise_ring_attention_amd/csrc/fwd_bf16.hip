@@ -19,9 +19,11 @@
 // contraction runs over keys, so a common permutation of both operands
 // leaves the sum unchanged).
 //
-// Memory pipeline.  Key/value tiles of BN keys are copied global -> LDS with
-// direct-to-LDS loads (no registers, no LDS store instructions) into a ring
-// of four stages: iteration t reads tiles t-1 .. t+1 and loads tile t+2.
+// Memory pipeline.  Key and value tiles of BN keys are copied global -> LDS
+// with direct-to-LDS loads (no registers, no LDS store instructions) into two
+// rings of four tiles.  Iteration t reads K tiles t, t+1 and V tiles t-1, t,
+// issues K tile t+3 and V tile t+2, and at its end waits only for the loads
+// issued one iteration earlier: every load has two iterations to land.
 // Rows are XOR-swizzled in 16-byte chunks so that both the 16-byte K reads (16 rows per LDS cycle) and the
 // V transpose reads (4 rows x 32 columns per half-wave) touch every bank
 // once.  Keys past the end of the block load a clamped valid row; the mask
@@ -69,11 +71,8 @@ struct FwdCfg {
   static constexpr int NT = NW * 64;         // threads per workgroup
   static constexpr int ROWB = D * 2;         // bytes per K or V row
   static constexpr int TILEB = BN * ROWB;    // bytes per K (or V) tile
-  static constexpr int STAGEB = 2 * TILEB;   // K tile then V tile
-  static constexpr int NSTAGE = 4;
-  static constexpr int LPW = STAGEB / (NW * 1024);  // 1 KiB loads per wave per tile
-  static_assert(STAGEB % (NW * 1024) == 0 && LPW >= 1, "tile must split into 1 KiB loads");
-  static_assert(TILEB % 1024 == 0, "a load must not straddle K and V");
+  static constexpr int NSLOT = 4;            // K ring and V ring, 4 tiles each
+  static constexpr int VBASE = NSLOT * TILEB;  // V ring after the K ring
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
 };
 
@@ -86,7 +85,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
   constexpr int KK = BN / 32;  // 32-key sub-tiles per tile
   constexpr int DS = D / 16;   // 16-wide head-dim slices (S contraction)
   constexpr int DD = D / 32;   // 32-wide head-dim tiles (O^T rows)
-  __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGEB];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::NSLOT * C::TILEB];
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lvoid*)smem;  // LDS byte address
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -117,13 +116,19 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
 
   const LdsOffsets<D> off(lane);
 
-  const StageLoader<D, BN, NW> loader(wave, lane);
-  auto issue_tile = [&](int t) __attribute__((always_inline)) {
-    loader.issue(smem_lds + (t % C::NSTAGE) * C::STAGEB, Kp, Vp, t * BN, Lk);
+  const TileLoader<D, BN, NW> loader(wave, lane);
+  auto issue_k = [&](int t) __attribute__((always_inline)) {
+    loader.issue(smem_lds + (t % C::NSLOT) * C::TILEB, Kp, t * BN, Lk);
+  };
+  auto issue_v = [&](int t) __attribute__((always_inline)) {
+    loader.issue(smem_lds + C::VBASE + (t % C::NSLOT) * C::TILEB, Vp, t * BN, Lk);
   };
 
-  if (ntiles > 0) issue_tile(0);
-  if (ntiles > 1) issue_tile(1);
+  // Iteration 0 needs K tiles 0, 1 and V tile 0; K 2 and V 1 may stay in
+  // flight until its end.
+  if (ntiles > 0) issue_k(0);
+  if (ntiles > 0) issue_v(0);
+  if (ntiles > 1) issue_k(1);
 
   // Queries of this wave: B operand of S^T = K Q^T.
   bf16x8 qreg[DS];
@@ -138,27 +143,28 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
   f32x16 s[KK];      // scores of the tile being softmaxed
   bf16x8 pb[KK][2];  // its probabilities, bf16, as PV B operands
 
-  // Iteration 0 reads tiles 0 and 1.
   wait_vmem();
+  if (ntiles > 2) issue_k(2);
+  if (ntiles > 1) issue_v(1);
   __syncthreads();
 
-  auto scores = [&](const char* stage) __attribute__((always_inline)) {  // s = K Q^T
+  auto scores = [&](const char* kt) __attribute__((always_inline)) {  // s = K Q^T
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) s[kk] = f32x16{};
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const bf16x8 a = *(const bf16x8*)(stage + kk * 32 * C::ROWB + off.row[ds]);
+        const bf16x8 a = *(const bf16x8*)(kt + kk * 32 * C::ROWB + off.row[ds]);
         s[kk] = mfma32(a, qreg[ds], s[kk]);
       }
   };
-  auto value = [&](const char* stage) __attribute__((always_inline)) {  // O^T += V^T P^T
+  auto value = [&](const char* vt) __attribute__((always_inline)) {  // O^T += V^T P^T
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const char* vb = stage + C::TILEB + (kk * 32 + 16 * half) * C::ROWB;
+        const char* vb = vt + (kk * 32 + 16 * half) * C::ROWB;
 #pragma unroll
         for (int dd = 0; dd < DD; ++dd) {
           const bf16x4 lo = lds_read_tr((const bf16*)(vb + off.tr[dd]));
@@ -196,63 +202,75 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
     const float negm = -m;
     float rs = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
+    for (int kk = 0; kk < KK; ++kk) {
+      f32x16 p;  // not written back into s: s is dead until the next scores
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2_fast(fmaf(s[kk][r], c2, negm));
-        s[kk][r] = p;
-        rs += p;
+        p[r] = exp2_fast(fmaf(s[kk][r], c2, negm));
+        rs += p[r];
       }
-    lsum += rs;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      pb[kk][0] = to_bf16x8(s[kk], 0);
-      pb[kk][1] = to_bf16x8(s[kk], 1);
+      pb[kk][0] = to_bf16x8(p, 0);
+      pb[kk][1] = to_bf16x8(p, 1);
     }
+    lsum += rs;
   };
 
-  auto stage_of = [&](int t) __attribute__((always_inline)) -> const char* {
-    return smem + (t % C::NSTAGE) * C::STAGEB;
+  auto k_of = [&](int t) __attribute__((always_inline)) -> const char* {
+    return smem + (t % C::NSLOT) * C::TILEB;
+  };
+  auto v_of = [&](int t) __attribute__((always_inline)) -> const char* {
+    return smem + C::VBASE + (t % C::NSLOT) * C::TILEB;
   };
 
   // Group A computes the scores of tile 0 before the loop; group B computes
   // the scores of tile t inside iteration t.
-  if (!group_b && ntw > 0) scores(stage_of(0));
+  if (!group_b && ntw > 0) scores(k_of(0));
 
   for (int t = 0; t < ntiles; ++t) {
-    if (t + 2 < ntiles) issue_tile(t + 2);
+    // K slot (t+3)%4 last served iteration t-1 (K tile t-1); V slot
+    // (t+2)%4 last served iteration t-1 (V tile t-2).
+    if (t + 3 < ntiles) issue_k(t + 3);
+    if (t + 2 < ntiles) issue_v(t + 2);
     if (!group_b) {
       // A: softmax(t), then value(t) + scores(t+1)
       if (t < ntw) {
         softmax(t);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(1);
-        value(stage_of(t));
-        if (t + 1 < ntw) scores(stage_of(t + 1));
+        value(v_of(t));
+        // Unconditional: past the wave's last tile the scores are unused, and
+        // a branch here would keep the previous tile's registers alive.
+        scores(k_of(t + 1));
         __builtin_amdgcn_s_setprio(0);
       }
     } else {
       // B: value(t-1) + scores(t), then softmax(t)
       if (t >= 1 && t - 1 < ntw) {
         __builtin_amdgcn_s_setprio(1);
-        value(stage_of(t - 1));
-        if (t < ntw) scores(stage_of(t));
+        value(v_of(t - 1));
+        scores(k_of(t));
         __builtin_amdgcn_s_setprio(0);
       } else if (t == 0 && ntw > 0) {
         __builtin_amdgcn_s_setprio(1);
-        scores(stage_of(0));
+        scores(k_of(0));
         __builtin_amdgcn_s_setprio(0);
       }
       __builtin_amdgcn_sched_barrier(0);
       if (t < ntw) softmax(t);
     }
-    // Iteration t+1 reads tile t+2 (group A's scores), issued above.
-    wait_vmem();
+    // Iteration t+1 reads K tile t+2 and V tile t+1 (issued in iteration
+    // t-1); this iteration's loads may stay in flight.
+    if (t + 3 < ntiles)
+      wait_vmem_n<2 * TileLoader<D, BN, NW>::LPW>();
+    else if (t + 2 < ntiles)
+      wait_vmem_n<TileLoader<D, BN, NW>::LPW>();
+    else
+      wait_vmem();
     __syncthreads();
   }
   // Group B still owes the value product of its last tile; no load touched
-  // that stage after the loop.
-  if (group_b && ntw == ntiles && ntw > 0) value(stage_of(ntw - 1));
+  // that V slot after the loop.
+  if (group_b && ntw == ntiles && ntw > 0) value(v_of(ntw - 1));
 
   // Fold the block partial into the running accumulators.
   const float ltot = add_halves(lsum);

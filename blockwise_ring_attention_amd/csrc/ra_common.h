@@ -111,11 +111,49 @@ __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32
                :: "v"(voff), "s"(sbase), "s"(lds_base) : "memory", "m0");
 }
 
+// Source offsets of the swizzled tile copies.  Load j of a tile moves bytes
+// [1024 j, 1024 j + 1024) of the LDS tile; lane l's 16 bytes come from
+// source byte offset
+//     1024 j + (lane_part(l) ^ (swz(1024 j / ROWB) << 4)),
+// where lane_part is the offset for j = 0.  This holds because every 1 KiB
+// covers whole rows (ROWB divides 1024) and the swizzle of row r + 1024j/ROWB
+// differs from that of r < 1024/ROWB by swz(1024j/ROWB) (XOR-linear in the
+// bits involved).  So a load costs one XOR with a wave-uniform value.
+template <int D>
+__device__ __forceinline__ uint32_t dma_lane_part(int lane) {
+  constexpr int ROWB = D * 2;
+  const int q = lane * 16;
+  const int row = q / ROWB;
+  return (uint32_t)(row * ROWB + ((((q % ROWB) >> 4) ^ swz<D>(row)) << 4));
+}
+template <int D>
+__device__ __forceinline__ uint32_t dma_xor(int j) {
+  return (uint32_t)(swz<D>(j * 1024 / (D * 2)) << 4);
+}
+
+// One 1 KiB load of a swizzled tile copy: load j (wave-uniform) of the tile
+// whose first row is row t0 of a [L x D] tensor A, into LDS byte address
+// tile_lds + 1024 j.  Rows past L-1 are clamped to L-1.
+template <int D, int BT>
+__device__ __forceinline__ void dma_tile_load(uint32_t tile_lds, const bf16* A, int t0, int L,
+                                              int j, uint32_t lane_part) {
+  constexpr int ROWB = D * 2;
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(tile_lds + (uint32_t)j * 1024);
+  if (t0 + BT <= L) {
+    // (x ^ y) + z is one v_xad_u32; the scalar base stays the tile's.
+    dma16_s(uniform(A + (size_t)t0 * D), (lane_part ^ dma_xor<D>(j)) + (uint32_t)j * 1024, lds);
+  } else {
+    const uint32_t off = lane_part ^ dma_xor<D>(j);
+    const int row = j * (1024 / ROWB) + (int)(off / ROWB);
+    dma16((const char*)(A + (size_t)min(t0 + row, L - 1) * D) + off % ROWB, lds);
+  }
+}
+
 // Copies one pipeline stage: two [BT x D] bf16 tiles (rows t0 .. t0+BT-1 of
 // tensors A and B, each [L x D]) into swizzled LDS rows, 1 KiB per wave
-// instruction.  Per-lane source offsets are fixed at construction; a tile
-// that runs past row L-1 takes a slower path that clamps rows to L-1 (the
-// caller masks them).
+// instruction, LPW instructions per wave.  For kernels short of registers
+// the lane offset is recomputed at each call (a few integer operations)
+// rather than held across the loop.
 template <int D, int BT, int NW>
 struct StageLoader {
   static constexpr int ROWB = D * 2;
@@ -124,31 +162,56 @@ struct StageLoader {
   static constexpr int LPW = STAGEB / (NW * 1024);
   static_assert(STAGEB % (NW * 1024) == 0 && LPW >= 1, "tile must split into 1 KiB loads");
   static_assert(TILEB % 1024 == 0, "a load must not straddle the two tiles");
-  int wave, lane;  // wave must be wave-uniform
+  int wave, lane;
   __device__ __forceinline__ StageLoader(int wave_, int lane_) : wave(wave_), lane(lane_) {}
   __device__ __forceinline__ void issue(uint32_t stage_lds, const bf16* A, const bf16* B, int t0,
                                         int L) const {
-    const bool full = t0 + BT <= L;
-    // Recompute the per-lane offsets at each call instead of letting them be
-    // hoisted into registers that live across the whole loop (they are a
-    // few integer operations; held registers have been spilled).
     int ln = lane;
-    asm volatile("" : "+v"(ln));
+    asm volatile("" : "+v"(ln));  // keep the offset from being hoisted out of the loop
+    const uint32_t lane_part = dma_lane_part<D>(ln);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      const int j = wave * LPW + i;
-      const int q = (j * 1024 + ln * 16) % TILEB;
-      const int row = q / ROWB;
-      const int lc = ((q % ROWB) >> 4) ^ swz<D>(row);
-      const bf16* base = (j * 1024) / TILEB ? B : A;
-      const uint32_t lds = __builtin_amdgcn_readfirstlane(stage_lds + j * 1024);
-      if (full)
-        dma16_s(uniform(base + (size_t)t0 * D), (uint32_t)(row * ROWB + lc * 16), lds);
+      const int j = wave * LPW + i;                // load index within the stage
+      constexpr int JT = TILEB / 1024;             // loads per tile
+      if (j < JT)
+        dma_tile_load<D, BT>(stage_lds, A, t0, L, j, lane_part);
       else
-        dma16(base + (size_t)min(t0 + row, L - 1) * D + lc * 8, lds);
+        dma_tile_load<D, BT>(stage_lds + TILEB, B, t0, L, j - JT, lane_part);
     }
   }
 };
+
+// Copies one [BT x D] bf16 tile (rows t0 .. t0+BT-1 of a [L x D] tensor)
+// into swizzled LDS rows with NL = TILEB / 1 KiB loads.  Either every wave
+// issues LPW = NL / NW of them, or (NL < NW) waves 0 .. NL-1 issue one each
+// and the rest none: a wave never has more than LPW loads per tile in
+// flight, which is what a kernel counts in vmcnt.
+template <int D, int BT, int NW>
+struct TileLoader {
+  static constexpr int ROWB = D * 2;
+  static constexpr int TILEB = BT * ROWB;
+  static constexpr int NL = TILEB / 1024;
+  static constexpr int LPW = NL >= NW ? NL / NW : 1;
+  static_assert(TILEB % 1024 == 0 && (NL % NW == 0 || NL < NW), "tile must split into 1 KiB loads");
+  int wave;            // wave-uniform
+  uint32_t lane_part;  // one register for every load
+  __device__ __forceinline__ TileLoader(int wave_, int lane)
+      : wave(__builtin_amdgcn_readfirstlane(wave_)), lane_part(dma_lane_part<D>(lane)) {}
+  __device__ __forceinline__ void issue(uint32_t tile_lds, const bf16* A, int t0, int L) const {
+    if (NL < NW && wave >= NL) return;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) dma_tile_load<D, BT>(tile_lds, A, t0, L, wave * LPW + i, lane_part);
+  }
+};
+
+// s_waitcnt vmcnt(N) with expcnt and lgkmcnt left at their maxima (gfx9
+// encoding: vmcnt bits [3:0] and [15:14]).  Vector memory loads complete in
+// issue order, so vmcnt(N) means all but the N most recent are done.
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 // s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maxima).  The builtin,
 // unlike inline asm, tells the compiler that earlier global loads are done.
