@@ -173,6 +173,9 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
         }
       }
   };
+  // value: KK*2*DD MFMAs with two transpose reads each; scores: DS*KK MFMAs
+  // with one 16-byte read each.
+  using Pipe = MfmaReadPipeline<KK * 2 * DD, 2, DS * KK, 1, 4>;
   auto softmax = [&](int t) __attribute__((always_inline)) {  // s (raw scores of tile t) -> pb, m, lsum
     const int kt0 = t * BN;
     // (wave-uniform; made scalar so the mask is a skipped branch, not selects)
@@ -241,6 +244,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
         // Unconditional: past the wave's last tile the scores are unused, and
         // a branch here would keep the previous tile's registers alive.
         scores(k_of(t + 1));
+        Pipe::apply();
         __builtin_amdgcn_s_setprio(0);
       }
     } else {
@@ -249,6 +253,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
         __builtin_amdgcn_s_setprio(1);
         value(v_of(t - 1));
         scores(k_of(t));
+        Pipe::apply();
         __builtin_amdgcn_s_setprio(0);
       } else if (t == 0 && ntw > 0) {
         __builtin_amdgcn_s_setprio(1);

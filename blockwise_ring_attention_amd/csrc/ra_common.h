@@ -204,6 +204,34 @@ struct TileLoader {
   }
 };
 
+// Scheduling hint for a run of NA MFMAs that take RA LDS reads each,
+// followed by NB MFMAs that take RB reads each (one basic block, reads in
+// the order of their use): the reads of the first LEAD MFMAs go first, then
+// each MFMA is followed by the reads of the MFMA LEAD places later.  Keeps
+// LDS latency off the MFMA chain without holding all operands at once.
+template <int NA, int RA, int NB, int RB, int LEAD>
+struct MfmaReadPipeline {
+  static constexpr int reads_of(int m) { return m < NA ? RA : (m < NA + NB ? RB : 0); }
+  template <int I>
+  static __device__ __forceinline__ void step() {
+    if constexpr (I < NA + NB) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      if constexpr (reads_of(I + LEAD) > 0)
+        __builtin_amdgcn_sched_group_barrier(0x100, reads_of(I + LEAD), 0);  // its reads
+      step<I + 1>();
+    }
+  }
+  template <int I>
+  static constexpr int lead_reads() {
+    if constexpr (I < LEAD) return reads_of(I) + lead_reads<I + 1>();
+    else return 0;
+  }
+  static __device__ __forceinline__ void apply() {
+    __builtin_amdgcn_sched_group_barrier(0x100, lead_reads<0>(), 0);
+    step<0>();
+  }
+};
+
 // s_waitcnt vmcnt(N) with expcnt and lgkmcnt left at their maxima (gfx9
 // encoding: vmcnt bits [3:0] and [15:14]).  Vector memory loads complete in
 // issue order, so vmcnt(N) means all but the N most recent are done.
