@@ -51,7 +51,11 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
   using C = TileCfg<D, BN, NW>;
   constexpr int BM = NW * 32;
   constexpr int KK = BN / 32, DS = D / 16, DD = D / 32;
-  __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGEB];
+  // K ring: iteration t reads K tiles t-1 .. t+1, has t+2 in flight and
+  // issues t+3.  V ring: reads t, t+1, t+2 in flight, issues t+3.
+  constexpr int NK = 5, NV = 4;
+  constexpr int VBASE = NK * C::TILEB;
+  __shared__ __attribute__((aligned(1024))) char smem[(NK + NV) * C::TILEB];
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lvoid*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -78,12 +82,21 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
   if (qw0 < Lq) ntw = diag ? min(ntiles, qw_last / BN + 1) : ntiles;
 
   const LdsOffsets<D> off(lane);
-  const StageLoader<D, BN, NW> loader(wave, lane);
-  auto issue = [&](int t) __attribute__((always_inline)) {
-    loader.issue(smem_lds + (t % C::NSTAGE) * C::STAGEB, Kp, Vp, t * BN, Lk);
+  using Loader = TileLoader<D, BN, NW, false>;
+  const Loader loader(wave, lane);
+  auto issue_k = [&](int t) __attribute__((always_inline)) {
+    loader.issue(smem_lds + (t % NK) * C::TILEB, Kp, t * BN, Lk);
   };
-  if (ntiles > 0) issue(0);
-  if (ntiles > 1) issue(1);
+  auto issue_v = [&](int t) __attribute__((always_inline)) {
+    loader.issue(smem_lds + VBASE + (t % NV) * C::TILEB, Vp, t * BN, Lk);
+  };
+  // Iteration 0 needs K and V tiles 0 and 1 (group A's scores of tile 1);
+  // tiles 2 may stay in flight until its end.
+  for (int t = 0; t < 2; ++t)
+    if (t < ntiles) {
+      issue_k(t);
+      issue_v(t);
+    }
 
   bf16x8 qreg[DS], doreg[DS];
 #pragma unroll
@@ -104,12 +117,19 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
   bf16x8 pb[KK][2];
 
   wait_vmem();
+  if (ntiles > 2) {
+    issue_k(2);
+    issue_v(2);
+  }
   __syncthreads();
 
-  auto stage_of = [&](int t) __attribute__((always_inline)) -> const char* {
-    return smem + (t % C::NSTAGE) * C::STAGEB;
+  auto k_of = [&](int t) __attribute__((always_inline)) -> const char* {
+    return smem + (t % NK) * C::TILEB;
   };
-  auto scores = [&](const char* st) __attribute__((always_inline)) {  // S^T, dP^T
+  auto v_of = [&](int t) __attribute__((always_inline)) -> const char* {
+    return smem + VBASE + (t % NV) * C::TILEB;
+  };
+  auto scores = [&](const char* kt, const char* vt) __attribute__((always_inline)) {  // S^T, dP^T
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       s[kk] = f32x16{};
@@ -119,9 +139,9 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
     for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const char* rb = st + kk * 32 * C::ROWB + off.row[ds];
-        s[kk] = mfma32(*(const bf16x8*)rb, qreg[ds], s[kk]);
-        dp[kk] = mfma32(*(const bf16x8*)(rb + C::TILEB), doreg[ds], dp[kk]);
+        const int ro = kk * 32 * C::ROWB + off.row[ds];
+        s[kk] = mfma32(*(const bf16x8*)(kt + ro), qreg[ds], s[kk]);
+        dp[kk] = mfma32(*(const bf16x8*)(vt + ro), doreg[ds], dp[kk]);
       }
   };
   auto grad = [&](int t) __attribute__((always_inline)) {  // dS^T -> pb
@@ -136,24 +156,23 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
         }
     }
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
+    for (int kk = 0; kk < KK; ++kk) {
+      f32x16 g;  // not written back into s: s is dead until the next scores
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = exp2_fast(fmaf(s[kk][r], c2, neg_lse2));
-        s[kk][r] = p * (dp[kk][r] - delta);
+        g[r] = p * (dp[kk][r] - delta);
       }
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      pb[kk][0] = to_bf16x8(s[kk], 0);
-      pb[kk][1] = to_bf16x8(s[kk], 1);
+      pb[kk][0] = to_bf16x8(g, 0);
+      pb[kk][1] = to_bf16x8(g, 1);
     }
   };
-  auto value = [&](const char* st) __attribute__((always_inline)) {  // dQ^T += K^T dS^T
+  auto value = [&](const char* kt) __attribute__((always_inline)) {  // dQ^T += K^T dS^T
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const char* kb = st + (kk * 32 + 16 * half) * C::ROWB;
+        const char* kb = kt + (kk * 32 + 16 * half) * C::ROWB;
 #pragma unroll
         for (int dd = 0; dd < DD; ++dd) {
           const bf16x4 lo = lds_read_tr((const bf16*)(kb + off.tr[dd]));
@@ -163,36 +182,55 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
       }
   };
 
-  if (!group_b && ntw > 0) scores(stage_of(0));
+  // value: KK*2*DD MFMAs with two transpose reads each; scores: DS*KK*2
+  // MFMAs with one 16-byte read each.
+  using Pipe = MfmaReadPipeline<KK * 2 * DD, 2, DS * KK * 2, 1, 4>;
+  if (!group_b && ntw > 0) scores(k_of(0), v_of(0));
   for (int t = 0; t < ntiles; ++t) {
-    if (t + 2 < ntiles) issue(t + 2);
+    // K slot (t+3)%5 last served iteration t-1 (K tile t-2, group B's
+    // value); V slot (t+3)%4 last served iteration t-1 (V tile t-1).
+    if (t + 3 < ntiles) {
+      issue_k(t + 3);
+      issue_v(t + 3);
+    }
     if (!group_b) {
       if (t < ntw) {
         grad(t);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(1);
-        value(stage_of(t));
-        if (t + 1 < ntw) scores(stage_of(t + 1));
+        value(k_of(t));
+        // Unconditional: past the wave's last tile the scores are unused, and
+        // a branch here would keep the previous tile's registers alive.
+        scores(k_of(t + 1), v_of(t + 1));
+        Pipe::apply();
         __builtin_amdgcn_s_setprio(0);
       }
     } else {
       if (t >= 1 && t - 1 < ntw) {
         __builtin_amdgcn_s_setprio(1);
-        value(stage_of(t - 1));
-        if (t < ntw) scores(stage_of(t));
+        value(k_of(t - 1));
+        scores(k_of(t), v_of(t));
+        Pipe::apply();
         __builtin_amdgcn_s_setprio(0);
       } else if (t == 0 && ntw > 0) {
         __builtin_amdgcn_s_setprio(1);
-        scores(stage_of(0));
+        scores(k_of(0), v_of(0));
         __builtin_amdgcn_s_setprio(0);
       }
       __builtin_amdgcn_sched_barrier(0);
       if (t < ntw) grad(t);
     }
-    wait_vmem();
+    // Iteration t+1 reads K and V tile t+2 (issued in iteration t-1); this
+    // iteration's loads may stay in flight.
+    if (t + 3 < ntiles)
+      wait_vmem_n<2 * Loader::LPW>();
+    else
+      wait_vmem();
     __syncthreads();
   }
-  if (group_b && ntw == ntiles && ntw > 0) value(stage_of(ntw - 1));
+  // Group B still owes the value product of its last tile; no load touched
+  // that K slot after the loop.
+  if (group_b && ntw == ntiles && ntw > 0) value(k_of(ntw - 1));
 
   if (qi < Lq) {
     float* row = dQacc + ((size_t)bh * Lq + qi) * D;

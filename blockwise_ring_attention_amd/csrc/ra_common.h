@@ -186,7 +186,9 @@ struct StageLoader {
 // issues LPW = NL / NW of them, or (NL < NW) waves 0 .. NL-1 issue one each
 // and the rest none: a wave never has more than LPW loads per tile in
 // flight, which is what a kernel counts in vmcnt.
-template <int D, int BT, int NW>
+// HOLD keeps the lane offset in a register across calls; otherwise it is
+// recomputed at each call (for kernels short of registers).
+template <int D, int BT, int NW, bool HOLD = true>
 struct TileLoader {
   static constexpr int ROWB = D * 2;
   static constexpr int TILEB = BT * ROWB;
@@ -194,13 +196,21 @@ struct TileLoader {
   static constexpr int LPW = NL >= NW ? NL / NW : 1;
   static_assert(TILEB % 1024 == 0 && (NL % NW == 0 || NL < NW), "tile must split into 1 KiB loads");
   int wave;            // wave-uniform
-  uint32_t lane_part;  // one register for every load
-  __device__ __forceinline__ TileLoader(int wave_, int lane)
-      : wave(__builtin_amdgcn_readfirstlane(wave_)), lane_part(dma_lane_part<D>(lane)) {}
+  int lane;
+  uint32_t lane_part;  // HOLD: one register for every load
+  __device__ __forceinline__ TileLoader(int wave_, int lane_)
+      : wave(__builtin_amdgcn_readfirstlane(wave_)), lane(lane_),
+        lane_part(HOLD ? dma_lane_part<D>(lane_) : 0u) {}
   __device__ __forceinline__ void issue(uint32_t tile_lds, const bf16* A, int t0, int L) const {
     if (NL < NW && wave >= NL) return;
+    uint32_t lp = lane_part;
+    if (!HOLD) {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));  // keep the offset from being hoisted out of the loop
+      lp = dma_lane_part<D>(ln);
+    }
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) dma_tile_load<D, BT>(tile_lds, A, t0, L, wave * LPW + i, lane_part);
+    for (int i = 0; i < LPW; ++i) dma_tile_load<D, BT>(tile_lds, A, t0, L, wave * LPW + i, lp);
   }
 };
 
