@@ -259,13 +259,16 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
   using C = TileCfg<D, BQ, NW>;
   constexpr int BK = NW * 32;  // keys per workgroup
   constexpr int DS = D / 16, DD = D / 32;
-  static_assert(BQ == 64, "two 32-query sub-tiles per LDS tile");
-  static_assert(2 * BQ <= C::NT, "one thread per lse / delta value");
+  static_assert(BQ == 64 && NW == 4, "two 32-query sub-tiles per LDS tile; one lse/delta load per wave");
   __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGEB];
-  __shared__ __attribute__((aligned(16))) float s_ld[C::NSTAGE][2][BQ];  // -lse*log2e, delta
+  // Per stage: row 0 lse (converted in place to -lse*log2e), row 1 delta,
+  // rows 2-3 written by the other two waves' copies and never read.
+  __shared__ __attribute__((aligned(1024))) float s_ld[C::NSTAGE][4][BQ];
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lvoid*)smem;
+  const uint32_t sld_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)&s_ld[0][0][0];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: loop bounds derive from it
   const int l32 = lane & 31, hl = lane >> 5;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / n_kt;
@@ -290,42 +293,43 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
   if (kw0 >= Lk) ft = ntiles;
 
   const LdsOffsets<D> off(lane);
-  const StageLoader<D, BQ, NW> loader(wave, lane);
+  using Loader = TileLoader<D, BQ, NW, false>;
+  const Loader loader(wave, lane);
+  // Per tile each wave issues LPW loads of Q, LPW of dO and one 256-byte
+  // copy of lse (waves 0, 2) or delta (waves 1, 3): VPT loads, counted in
+  // vmcnt.  Iteration t reads stages t and t+1, has t+2 in flight and
+  // issues t+3 into the slot of tile t-1.
+  constexpr int VPT = 2 * Loader::LPW + 1;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   auto issue = [&](int t) __attribute__((always_inline)) {
-    loader.issue(smem_lds + (t % C::NSTAGE) * C::STAGEB, Qp, dOp, qstart + t * BQ, Lq);
+    const int st = t % C::NSTAGE;
+    const int q0t = qstart + t * BQ;
+    loader.issue(smem_lds + st * C::STAGEB, Qp, q0t, Lq);
+    loader.issue(smem_lds + st * C::STAGEB + C::TILEB, dOp, q0t, Lq);
+    dma4((wave_u & 1 ? Dp : Lp) + min(q0t + lane, Lq - 1), sld_lds + (st * 4 + wave_u) * BQ * 4);
   };
-  // lse / delta of a query tile: thread i < BQ loads lse, BQ <= i < 2BQ
-  // delta (whole waves, so no divergence); the raw value waits in a register
-  // while the iteration's loads are in flight and is converted on the store.
-  float ld_reg = 0.f;
-  auto load_ld = [&](int t) __attribute__((always_inline)) {
-    if (tid < 2 * BQ) {
-      const int q = min(qstart + t * BQ + (tid % BQ), Lq - 1);
-      ld_reg = (tid < BQ ? Lp : Dp)[q];
-    }
+  // In-place conversion of a landed tile's lse / delta (waves 0 and 1, one
+  // value per lane): lse -> -lse*log2e, with -inf (a row that saw no key, or
+  // past the end) giving P = 0; delta past the end -> 0.  The read is issued
+  // early and the write late in an iteration.
+  float ld_raw = 0.f;
+  auto ld_read = [&](int t) __attribute__((always_inline)) {
+    if (wave_u < 2) ld_raw = s_ld[t % C::NSTAGE][wave_u][lane];
   };
-  auto store_ld = [&](int t) __attribute__((always_inline)) {
-    if (tid < 2 * BQ) {
-      const bool valid = qstart + t * BQ + (tid % BQ) < Lq;
+  auto ld_write = [&](int t) __attribute__((always_inline)) {
+    if (wave_u < 2) {
+      const bool valid = qstart + t * BQ + lane < Lq;
       float v;
-      if (tid < BQ)  // negated lse in log2 units; -inf (dead or past the end): P = 0
-        v = (!valid || ld_reg == -INFINITY) ? -INFINITY : -ld_reg * kLog2e;
+      if (wave_u == 0)
+        v = (!valid || ld_raw == -INFINITY) ? -INFINITY : -ld_raw * kLog2e;
       else
-        v = valid ? ld_reg : 0.f;
-      s_ld[t % C::NSTAGE][tid / BQ][tid % BQ] = v;
+        v = valid ? ld_raw : 0.f;
+      s_ld[t % C::NSTAGE][wave_u][lane] = v;
     }
   };
 
-  if (ntiles > 0) {
-    issue(0);
-    load_ld(0);
-    store_ld(0);
-  }
-  if (ntiles > 1) {
-    issue(1);
-    load_ld(1);
-    store_ld(1);
-  }
+  if (ntiles > 0) issue(0);
+  if (ntiles > 1) issue(1);
 
   bf16x8 kreg[DS], vreg[DS];
 #pragma unroll
@@ -345,6 +349,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
   bf16x8 ob[2][8];         // LDS operands, one MFMA step ahead
 
   wait_vmem();
+  __syncthreads();
+  if (ntiles > 0) {
+    ld_read(0);
+    ld_write(0);
+  }
+  if (ntiles > 2) issue(2);
   __syncthreads();
 
   auto stage_of = [&](int t) __attribute__((always_inline)) -> const char* {
@@ -448,15 +458,18 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
     steps(0, 2, stage_of(t), qs, nullptr, 0);
   };
   auto end_tile = [&](int t) __attribute__((always_inline)) {
-    if (t + 2 < ntiles) store_ld(t + 2);
-    wait_vmem();
+    if (t + 1 < ntiles) ld_write(t + 1);
+    // Iteration t+1 reads stage t+2 (issued in iteration t-1); this
+    // iteration's loads may stay in flight.
+    if (t + 3 < ntiles)
+      wait_vmem_n<VPT>();
+    else
+      wait_vmem();
     __syncthreads();
   };
   auto begin_tile = [&](int t) __attribute__((always_inline)) {
-    if (t + 2 < ntiles) {
-      issue(t + 2);
-      load_ld(t + 2);
-    }
+    if (t + 3 < ntiles) issue(t + 3);
+    if (t + 1 < ntiles) ld_read(t + 1);
   };
 
   // Tiles before this wave's first active tile: only keep the pipeline

@@ -95,6 +95,13 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
                :: "v"(src), "s"(lds_base) : "memory", "m0");
 }
 
+// Direct-to-LDS copy of 4 bytes per lane: lane l's word lands at LDS byte
+// address lds_base + 4*l.  Same contract as dma16.
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base)) : "memory", "m0");
+}
+
 // A pointer the caller knows to be wave-uniform, moved to scalar registers.
 template <typename T>
 __device__ __forceinline__ T* uniform(T* p) {
@@ -131,55 +138,34 @@ __device__ __forceinline__ uint32_t dma_xor(int j) {
   return (uint32_t)(swz<D>(j * 1024 / (D * 2)) << 4);
 }
 
-// One 1 KiB load of a swizzled tile copy: load j (wave-uniform) of the tile
-// whose first row is row t0 of a [L x D] tensor A, into LDS byte address
-// tile_lds + 1024 j.  Rows past L-1 are clamped to L-1.
-template <int D, int BT>
-__device__ __forceinline__ void dma_tile_load(uint32_t tile_lds, const bf16* A, int t0, int L,
-                                              int j, uint32_t lane_part) {
+// Loads j0 .. j0+N-1 of a swizzled tile copy (j0 wave-uniform): the tile's
+// first row is row t0 of a [L x D] tensor A; load j fills LDS bytes
+// tile_lds + 1024 j ... + 1023.  One scalar branch per call picks the full
+// tile form (scalar base + one XOR-add per load) or the ragged form (rows
+// past L-1 clamped to L-1).
+template <int D, int BT, int N>
+__device__ __forceinline__ void dma_tile_loads(uint32_t tile_lds, const bf16* A, int t0, int L,
+                                               int j0, uint32_t lane_part) {
   constexpr int ROWB = D * 2;
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(tile_lds + (uint32_t)j * 1024);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(tile_lds + (uint32_t)j0 * 1024);
   if (t0 + BT <= L) {
-    // (x ^ y) + z is one v_xad_u32; the scalar base stays the tile's.
-    dma16_s(uniform(A + (size_t)t0 * D), (lane_part ^ dma_xor<D>(j)) + (uint32_t)j * 1024, lds);
-  } else {
-    const uint32_t off = lane_part ^ dma_xor<D>(j);
-    const int row = j * (1024 / ROWB) + (int)(off / ROWB);
-    dma16((const char*)(A + (size_t)min(t0 + row, L - 1) * D) + off % ROWB, lds);
-  }
-}
-
-// Copies one pipeline stage: two [BT x D] bf16 tiles (rows t0 .. t0+BT-1 of
-// tensors A and B, each [L x D]) into swizzled LDS rows, 1 KiB per wave
-// instruction, LPW instructions per wave.  For kernels short of registers
-// the lane offset is recomputed at each call (a few integer operations)
-// rather than held across the loop.
-template <int D, int BT, int NW>
-struct StageLoader {
-  static constexpr int ROWB = D * 2;
-  static constexpr int TILEB = BT * ROWB;
-  static constexpr int STAGEB = 2 * TILEB;
-  static constexpr int LPW = STAGEB / (NW * 1024);
-  static_assert(STAGEB % (NW * 1024) == 0 && LPW >= 1, "tile must split into 1 KiB loads");
-  static_assert(TILEB % 1024 == 0, "a load must not straddle the two tiles");
-  int wave, lane;
-  __device__ __forceinline__ StageLoader(int wave_, int lane_) : wave(wave_), lane(lane_) {}
-  __device__ __forceinline__ void issue(uint32_t stage_lds, const bf16* A, const bf16* B, int t0,
-                                        int L) const {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));  // keep the offset from being hoisted out of the loop
-    const uint32_t lane_part = dma_lane_part<D>(ln);
+    const bf16* base = uniform(A + (size_t)t0 * D);
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int j = wave * LPW + i;                // load index within the stage
-      constexpr int JT = TILEB / 1024;             // loads per tile
-      if (j < JT)
-        dma_tile_load<D, BT>(stage_lds, A, t0, L, j, lane_part);
-      else
-        dma_tile_load<D, BT>(stage_lds + TILEB, B, t0, L, j - JT, lane_part);
+    for (int i = 0; i < N; ++i) {
+      const int j = j0 + i;
+      // (x ^ y) + z is one v_xad_u32
+      dma16_s(base, (lane_part ^ dma_xor<D>(j)) + (uint32_t)j * 1024, lds0 + i * 1024);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int j = j0 + i;
+      const uint32_t off = lane_part ^ dma_xor<D>(j);
+      const int row = j * (1024 / ROWB) + (int)(off / ROWB);
+      dma16((const char*)(A + (size_t)min(t0 + row, L - 1) * D) + off % ROWB, lds0 + i * 1024);
     }
   }
-};
+}
 
 // Copies one [BT x D] bf16 tile (rows t0 .. t0+BT-1 of a [L x D] tensor)
 // into swizzled LDS rows with NL = TILEB / 1 KiB loads.  Either every wave
@@ -209,8 +195,7 @@ struct TileLoader {
       asm volatile("" : "+v"(ln));  // keep the offset from being hoisted out of the loop
       lp = dma_lane_part<D>(ln);
     }
-#pragma unroll
-    for (int i = 0; i < LPW; ++i) dma_tile_load<D, BT>(tile_lds, A, t0, L, wave * LPW + i, lp);
+    dma_tile_loads<D, BT, LPW>(tile_lds, A, t0, L, wave * LPW, lp);
   }
 };
 
