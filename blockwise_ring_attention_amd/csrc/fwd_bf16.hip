@@ -116,7 +116,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
 
   const LdsOffsets<D> off(lane);
 
-  const TileLoader<D, BN, NW> loader(wave, lane);
+  const TileLoader<D, BN, NW, true, true> loader(wave, lane);
   auto issue_k = [&](int t) __attribute__((always_inline)) {
     loader.issue(smem_lds + (t % C::NSLOT) * C::TILEB, Kp, t * BN, Lk);
   };
@@ -266,9 +266,9 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
     // Iteration t+1 reads K tile t+2 and V tile t+1 (issued in iteration
     // t-1); this iteration's loads may stay in flight.
     if (t + 3 < ntiles)
-      wait_vmem_n<2 * TileLoader<D, BN, NW>::LPW>();
+      wait_vmem_n<2 * decltype(loader)::LPW>();
     else if (t + 2 < ntiles)
-      wait_vmem_n<TileLoader<D, BN, NW>::LPW>();
+      wait_vmem_n<decltype(loader)::LPW>();
     else
       wait_vmem();
     __syncthreads();

@@ -95,6 +95,33 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
                :: "v"(src), "s"(lds_base) : "memory", "m0");
 }
 
+// N consecutive 1 KiB direct-to-LDS copies from a wave-uniform base: copy i
+// reads 16 bytes per lane at sbase + voff[i] + 1024 i and writes them to LDS
+// byte address lds_base + 1024 i + 16*lane.  The instruction offset applies to
+// both the global and the LDS address, so M0 is written once for the group.
+template <int N>
+__device__ __forceinline__ void dma16_group(const void* sbase, const uint32_t (&voff)[N],
+                                            uint32_t lds_base) {
+  static_assert(N == 1 || N == 2 || N == 4, "group size");
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
+  if constexpr (N == 1)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff[0]), "s"(sbase), "s"(m0) : "memory", "m0");
+  else if constexpr (N == 2)
+    asm volatile("s_mov_b32 m0, %3\n\t"
+                 "global_load_lds_dwordx4 %0, %2\n\t"
+                 "global_load_lds_dwordx4 %1, %2 offset:1024"
+                 :: "v"(voff[0]), "v"(voff[1]), "s"(sbase), "s"(m0) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %5\n\t"
+                 "global_load_lds_dwordx4 %0, %4\n\t"
+                 "global_load_lds_dwordx4 %1, %4 offset:1024\n\t"
+                 "global_load_lds_dwordx4 %2, %4 offset:2048\n\t"
+                 "global_load_lds_dwordx4 %3, %4 offset:3072"
+                 :: "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(sbase), "s"(m0)
+                 : "memory", "m0");
+}
+
 // Direct-to-LDS copy of 4 bytes per lane: lane l's word lands at LDS byte
 // address lds_base + 4*l.  Same contract as dma16.
 __device__ __forceinline__ void dma4(const void* src, uint32_t lds_base) {
@@ -111,12 +138,6 @@ __device__ __forceinline__ T* uniform(T* p) {
   return (T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Same copy with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
-// byte offset (the global_load saddr form): no per-lane address arithmetic.
-__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(sbase), "s"(lds_base) : "memory", "m0");
-}
 
 // Source offsets of the swizzled tile copies.  Load j of a tile moves bytes
 // [1024 j, 1024 j + 1024) of the LDS tile; lane l's 16 bytes come from
@@ -143,19 +164,37 @@ __device__ __forceinline__ uint32_t dma_xor(int j) {
 // tile_lds + 1024 j ... + 1023.  One scalar branch per call picks the full
 // tile form (scalar base + one XOR-add per load) or the ragged form (rows
 // past L-1 clamped to L-1).
+// The same loads, each under its own full / ragged test with its own M0.
+// Same effect; which form schedules better depends on the kernel.
+template <int D, int BT, int N>
+__device__ __forceinline__ void dma_tile_loads_split(uint32_t tile_lds, const bf16* A, int t0,
+                                                     int L, int j0, uint32_t lane_part) {
+  constexpr int ROWB = D * 2;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int j = j0 + i;
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(tile_lds + (uint32_t)j * 1024);
+    const uint32_t off = lane_part ^ dma_xor<D>(j);
+    if (t0 + BT <= L) {
+      const uint32_t voff[1] = {off + (uint32_t)j * 1024};
+      dma16_group<1>(uniform(A + (size_t)t0 * D), voff, lds);
+    } else {
+      const int row = j * (1024 / ROWB) + (int)(off / ROWB);
+      dma16((const char*)(A + (size_t)min(t0 + row, L - 1) * D) + off % ROWB, lds);
+    }
+  }
+}
+
 template <int D, int BT, int N>
 __device__ __forceinline__ void dma_tile_loads(uint32_t tile_lds, const bf16* A, int t0, int L,
                                                int j0, uint32_t lane_part) {
   constexpr int ROWB = D * 2;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(tile_lds + (uint32_t)j0 * 1024);
   if (t0 + BT <= L) {
-    const bf16* base = uniform(A + (size_t)t0 * D);
+    uint32_t voff[N];  // (x ^ y) + z: one v_xad_u32 each
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int j = j0 + i;
-      // (x ^ y) + z is one v_xad_u32
-      dma16_s(base, (lane_part ^ dma_xor<D>(j)) + (uint32_t)j * 1024, lds0 + i * 1024);
-    }
+    for (int i = 0; i < N; ++i) voff[i] = (lane_part ^ dma_xor<D>(j0 + i)) + (uint32_t)j0 * 1024;
+    dma16_group<N>(uniform(A + (size_t)t0 * D), voff, lds0);
   } else {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
@@ -173,8 +212,10 @@ __device__ __forceinline__ void dma_tile_loads(uint32_t tile_lds, const bf16* A,
 // and the rest none: a wave never has more than LPW loads per tile in
 // flight, which is what a kernel counts in vmcnt.
 // HOLD keeps the lane offset in a register across calls; otherwise it is
-// recomputed at each call (for kernels short of registers).
-template <int D, int BT, int NW, bool HOLD = true>
+// recomputed at each call (for kernels short of registers).  SPLIT issues
+// each load under its own full / ragged test (dma_tile_loads_split), which
+// measured faster in the forward kernel; otherwise one test per call.
+template <int D, int BT, int NW, bool HOLD = true, bool SPLIT = false>
 struct TileLoader {
   static constexpr int ROWB = D * 2;
   static constexpr int TILEB = BT * ROWB;
@@ -195,7 +236,10 @@ struct TileLoader {
       asm volatile("" : "+v"(ln));  // keep the offset from being hoisted out of the loop
       lp = dma_lane_part<D>(ln);
     }
-    dma_tile_loads<D, BT, LPW>(tile_lds, A, t0, L, wave * LPW, lp);
+    if constexpr (SPLIT)
+      dma_tile_loads_split<D, BT, LPW>(tile_lds, A, t0, L, wave * LPW, lp);
+    else
+      dma_tile_loads<D, BT, LPW>(tile_lds, A, t0, L, wave * LPW, lp);
   }
 };
 
