@@ -31,6 +31,12 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wno-inline-as
          "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
+# Per-source flags.  The backward kernels keep the MFMA results that vector
+# code reads (scores) in VGPRs; their long-lived accumulators are placed in
+# AGPRs explicitly (inline asm), so the MFMA builtins are told to use VGPRs.
+SOURCE_FLAGS = {"bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -60,7 +66,8 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmds.append([hipcc, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, *FLAGS, *SOURCE_FLAGS.get(src, []), *lang, "-c",
+                     os.path.join(CSRC, src), "-o", obj])
     jobs = jobs or min(len(cmds), max(1, (os.cpu_count() or 2)))
     with ThreadPoolExecutor(jobs) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:

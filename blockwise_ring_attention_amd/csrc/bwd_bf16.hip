@@ -250,6 +250,24 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
 }
 
 // --------------------------------------------------------------- dK, dV ---
+// Key-major.  A wave owns 32 keys (K, V rows in registers) and walks the
+// query tiles of its block in 32-query sub-tiles n = 0, 1, 2, ... (two per
+// 64-query LDS tile).  Per sub-tile:
+//     scores(n):   S = Q K^T, dP = dO V^T             (16 MFMAs, row reads)
+//     grad(n):     P = exp2(S*c2 - lse*log2e), dS = P (dP - delta)   (VALU)
+//     products(n): dV += P^T dO, dK += dS^T Q         (16 MFMAs, transpose reads)
+// With one wave per SIMD the only overlap is within the wave, so the work is
+// software-pipelined: step n issues scores(n), then products(n-1) with the
+// VALU work of grad(n) interleaved between its MFMAs.  P and dS alternate
+// between two register sets (grad(n) writes one while products(n-1) reads the
+// other).
+//
+// Memory pipeline: four LDS stages of (Q tile, dO tile).  Iteration t (steps
+// 2t, 2t+1) reads stages t-1 (products(2t-1)) and t, issues tile t+2 into the
+// slot of tile t-2, and at its end waits for tile t+1 only.  Each wave keeps
+// a private copy of the tile's lse / delta rows (two 4-byte direct-to-LDS
+// copies) and converts it in place at the start of the iteration that uses
+// it, so no extra barrier is needed.
 template <int D, int BQ, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ KV,
@@ -259,13 +277,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
   using C = TileCfg<D, BQ, NW>;
   constexpr int BK = NW * 32;  // keys per workgroup
   constexpr int DS = D / 16, DD = D / 32;
-  static_assert(BQ == 64 && NW == 4, "two 32-query sub-tiles per LDS tile; one lse/delta load per wave");
+  static_assert(BQ == 64, "two 32-query sub-tiles per LDS tile");
   __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGEB];
-  // Per stage: row 0 lse (converted in place to -lse*log2e), row 1 delta,
-  // rows 2-3 written by the other two waves' copies and never read.
-  __shared__ __attribute__((aligned(1024))) float s_ld[C::NSTAGE][4][BQ];
+  // Per stage and wave: row 0 lse (converted in place to -lse*log2e), row 1 delta.
+  __shared__ __attribute__((aligned(1024))) float s_ld[C::NSTAGE][NW][2][BQ];
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lvoid*)smem;
-  const uint32_t sld_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)&s_ld[0][0][0];
+  const uint32_t sld_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)&s_ld[0][0][0][0];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: loop bounds derive from it
@@ -293,39 +310,30 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
   if (kw0 >= Lk) ft = ntiles;
 
   const LdsOffsets<D> off(lane);
-  using Loader = TileLoader<D, BQ, NW, false>;
+  using Loader = TileLoader<D, BQ, NW>;
   const Loader loader(wave, lane);
-  // Per tile each wave issues LPW loads of Q, LPW of dO and one 256-byte
-  // copy of lse (waves 0, 2) or delta (waves 1, 3): VPT loads, counted in
-  // vmcnt.  Iteration t reads stages t and t+1, has t+2 in flight and
-  // issues t+3 into the slot of tile t-1.
-  constexpr int VPT = 2 * Loader::LPW + 1;
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // Per tile each wave issues LPW loads of Q, LPW of dO and its own lse and
+  // delta rows: VPT loads, counted in vmcnt.
+  constexpr int VPT = 2 * Loader::LPW + 2;
   auto issue = [&](int t) __attribute__((always_inline)) {
     const int st = t % C::NSTAGE;
     const int q0t = qstart + t * BQ;
     loader.issue(smem_lds + st * C::STAGEB, Qp, q0t, Lq);
     loader.issue(smem_lds + st * C::STAGEB + C::TILEB, dOp, q0t, Lq);
-    dma4((wave_u & 1 ? Dp : Lp) + min(q0t + lane, Lq - 1), sld_lds + (st * 4 + wave_u) * BQ * 4);
+    const int q = min(q0t + lane, Lq - 1);
+    const uint32_t row = sld_lds + (uint32_t)((st * NW + wave) * 2 * BQ * 4);
+    dma4(Lp + q, row);
+    dma4(Dp + q, row + BQ * 4);
   };
-  // In-place conversion of a landed tile's lse / delta (waves 0 and 1, one
-  // value per lane): lse -> -lse*log2e, with -inf (a row that saw no key, or
-  // past the end) giving P = 0; delta past the end -> 0.  The read is issued
-  // early and the write late in an iteration.
-  float ld_raw = 0.f;
-  auto ld_read = [&](int t) __attribute__((always_inline)) {
-    if (wave_u < 2) ld_raw = s_ld[t % C::NSTAGE][wave_u][lane];
-  };
-  auto ld_write = [&](int t) __attribute__((always_inline)) {
-    if (wave_u < 2) {
-      const bool valid = qstart + t * BQ + lane < Lq;
-      float v;
-      if (wave_u == 0)
-        v = (!valid || ld_raw == -INFINITY) ? -INFINITY : -ld_raw * kLog2e;
-      else
-        v = valid ? ld_raw : 0.f;
-      s_ld[t % C::NSTAGE][wave_u][lane] = v;
-    }
+  // In-place conversion of this wave's copy for tile t (one lse and one
+  // delta per lane): lse -> -lse*log2e, where -inf (a row that saw no key)
+  // and rows past the end give P = 0; delta past the end -> 0.
+  auto convert_ld = [&](int t) __attribute__((always_inline)) {
+    float* row = &s_ld[t % C::NSTAGE][wave][0][0];
+    const bool valid = qstart + t * BQ + lane < Lq;
+    const float l = row[lane], d = row[BQ + lane];
+    row[lane] = (!valid || l == -INFINITY) ? -INFINITY : -l * kLog2e;
+    row[BQ + lane] = valid ? d : 0.f;
   };
 
   if (ntiles > 0) issue(0);
@@ -343,158 +351,169 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
     dk[dd] = f32x16{};
     dv[dd] = f32x16{};
   }
-  // Work runs in 32-query sub-tiles (qs = 0, 1) of the 64-query LDS tiles.
-  f32x16 s, dp;            // S and dP of the sub-tile to be softmaxed next
-  bf16x8 pbf[2], dsbf[2];  // P and dS of the sub-tile being multiplied
-  bf16x8 ob[2][8];         // LDS operands, one MFMA step ahead
+  f32x16 s, dp;               // S and dP of the newest scored sub-tile
+  bf16x8 pbf[2][2], dsbf[2][2];  // P and dS of two sub-tiles ([set][16-query half])
 
   wait_vmem();
-  __syncthreads();
-  if (ntiles > 0) {
-    ld_read(0);
-    ld_write(0);
-  }
-  if (ntiles > 2) issue(2);
   __syncthreads();
 
   auto stage_of = [&](int t) __attribute__((always_inline)) -> const char* {
     return smem + (t % C::NSTAGE) * C::STAGEB;
   };
-  // P = exp(S*scale - lse), dS = P (dP - delta) for sub-tile qs of tile t.
-  auto grad = [&](int t, int qs) __attribute__((always_inline)) {
+  // S = Q K^T and dP = dO V^T of sub-tile (t, qs).
+  auto scores = [&](int t, int qs) __attribute__((always_inline)) {
+    const char* st = stage_of(t) + qs * 32 * C::ROWB;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      const bf16x8 aq = *(const bf16x8*)(st + off.row[ds]);
+      const bf16x8 ado = *(const bf16x8*)(st + C::TILEB + off.row[ds]);
+      s = mfma32(aq, kreg[ds], ds == 0 ? f32x16{} : s);
+      dp = mfma32(ado, vreg[ds], ds == 0 ? f32x16{} : dp);
+    }
+  };
+  // Operand of product MFMA i of sub-tile (t, qs): i = 2*(DD*p + dd) + w,
+  // p the 16-query half, w = 0 the dO^T operand of dV[dd], w = 1 the Q^T
+  // operand of dK[dd] (transpose reads).
+  auto prod_operand = [&](int t, int qs, int i) __attribute__((always_inline)) -> bf16x8 {
+    const int p = i / (2 * DD), dd = (i / 2) % DD, w = i & 1;
+    const char* b = stage_of(t) + (qs * 32 + 16 * p) * C::ROWB + (w == 0 ? C::TILEB : 0);
+    return cat(lds_read_tr((const bf16*)(b + off.tr[dd])),
+               lds_read_tr((const bf16*)(b + off.tr[dd] + off.trd)));
+  };
+  f32x4 nl[4], dl[4];  // -lse*log2e and delta of the 16 query rows a lane holds
+  // The second half of a step, scheduled by hand in 16 chunks separated by
+  // scheduling barriers: chunk i issues product MFMA i of sub-tile (pt, pqs)
+  // (P / dS from set pset; dV, dK accumulate in AGPRs, see mfma32_acc), the
+  // transpose reads of product MFMA i + LEAD, and the vector work of element
+  // i of the gradient of the newest scores (exp2 of element i, dS and the
+  // bf16 rounding of element i - 1) into set gset.
+  auto prod_grad = [&](bool prod, int pt, int pqs, int pset, bool dograd, int gt, int gqs,
+                       int gset) __attribute__((always_inline)) {
+    constexpr int NP = 2 * 2 * DD, LEAD = 4;
+    if (dograd) {
+      const float* row = &s_ld[gt % C::NSTAGE][wave][0][0];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        nl[g] = *(const f32x4*)&row[gqs * 32 + 8 * g + 4 * hl];
+        dl[g] = *(const f32x4*)&row[BQ + gqs * 32 + 8 * g + 4 * hl];
+      }
+    }
+    bf16x8 op[NP];
+    if (prod) {
+#pragma unroll
+      for (int i = 0; i < LEAD; ++i) op[i] = prod_operand(pt, pqs, i);
+    }
+    f32x16 pr, dsr;
+    u32x4 pw[2], dw[2];
+    auto finish = [&](int r) __attribute__((always_inline)) {  // dS and rounding of element r
+      dsr[r] = pr[r] * (dp[r] - dl[r >> 2][r & 3]);
+      if (r & 1) {
+        const bf16x2 pp = {(bf16)pr[r - 1], (bf16)pr[r]};
+        const bf16x2 dq2 = {(bf16)dsr[r - 1], (bf16)dsr[r]};
+        pw[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pp);
+        dw[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, dq2);
+      }
+    };
+    // 16 gradient elements per lane; with fewer product MFMAs (D = 64) a
+    // chunk without an MFMA carries only gradient work.
+    constexpr int NCH = NP > 16 ? NP : 16, PER = NCH / NP;
+    static_assert(NCH == 16 && NCH % NP == 0, "chunking");
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if (prod && c % PER == 0) {
+        const int i = c / PER;
+        const int p = i / (2 * DD), dd = (i / 2) % DD;
+        if ((i & 1) == 0)
+          mfma32_acc(dv[dd], pbf[pset][p], op[i]);
+        else
+          mfma32_acc(dk[dd], dsbf[pset][p], op[i]);
+        if (i + LEAD < NP) op[i + LEAD] = prod_operand(pt, pqs, i + LEAD);
+      }
+      if (dograd) {
+        pr[c] = exp2_fast(fmaf(s[c], c2, nl[c >> 2][c & 3]));
+        if (c > 0) finish(c - 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (dograd) {
+      finish(NCH - 1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        pbf[gset][h] = __builtin_bit_cast(bf16x8, pw[h]);
+        dsbf[gset][h] = __builtin_bit_cast(bf16x8, dw[h]);
+      }
+    }
+  };
+  // Keys past the end, or after the query on the diagonal block, take no
+  // part: their P and dS (already rounded to bf16) are cleared bit-wise, which
+  // also discards any overflow in them.  Only sub-tiles that straddle the
+  // diagonal or the end of the block need it; the test is wave-uniform and
+  // made scalar, so elsewhere the mask is a skipped branch.
+  auto mask_grad = [&](int t, int qs, int set) __attribute__((always_inline)) {
     const int qt0 = qstart + t * BQ + qs * 32;
-    const int st = t % C::NSTAGE;
-    f32x4 nl[4], dl[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      nl[g] = *(const f32x4*)&s_ld[st][0][qs * 32 + 8 * g + 4 * hl];
-      dl[g] = *(const f32x4*)&s_ld[st][1][qs * 32 + 8 * g + 4 * hl];
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = exp2_fast(fmaf(s[r], c2, nl[r >> 2][r & 3]));
     if (__builtin_amdgcn_readfirstlane((kw0 + 31 >= Lk) || (diag && kw_last > qt0))) {
+      auto dead = [&](int r) { return kj >= Lk || (diag && kj > qt0 + 8 * (r >> 2) + 4 * hl + (r & 3)); };
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = qt0 + 8 * (r >> 2) + 4 * hl + (r & 3);
-        if (kj >= Lk || (diag && kj > q)) s[r] = 0.f;
-      }
-    }
+      for (int half = 0; half < 2; ++half) {
+        u32x4 pw = __builtin_bit_cast(u32x4, pbf[set][half]);
+        u32x4 dw = __builtin_bit_cast(u32x4, dsbf[set][half]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] - dl[r >> 2][r & 3]);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      pbf[half] = to_bf16x8(s, half);
-      dsbf[half] = to_bf16x8(dp, half);
-    }
-  };
-  // MFMA steps of 8.  Product steps p = 0, 1 (rows 16*p of the sub-tile):
-  // dV += P^T dO and dK += dS^T Q over the head-dim tiles, operands by
-  // transpose reads.  Score steps p = 2, 3 (head-dim slices (p-2)*DS/2 ..):
-  // S = Q K^T and dP = dO V^T, operands by 16-byte row reads; step 2 starts
-  // the accumulators from zero.
-  auto load_step = [&](int p, const char* st, int qs, bf16x8* o) __attribute__((always_inline)) {
-    if (p < 2) {
-      const char* qb = st + (qs * 32 + 16 * p) * C::ROWB;
-#pragma unroll
-      for (int dd = 0; dd < DD; ++dd) {
-        o[2 * dd] = cat(lds_read_tr((const bf16*)(qb + C::TILEB + off.tr[dd])),
-                        lds_read_tr((const bf16*)(qb + C::TILEB + off.tr[dd] + off.trd)));
-        o[2 * dd + 1] = cat(lds_read_tr((const bf16*)(qb + off.tr[dd])),
-                            lds_read_tr((const bf16*)(qb + off.tr[dd] + off.trd)));
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < DS / 2; ++j) {
-        const char* rb = st + qs * 32 * C::ROWB + off.row[(DS / 2) * (p - 2) + j];
-        o[2 * j] = *(const bf16x8*)rb;
-        o[2 * j + 1] = *(const bf16x8*)(rb + C::TILEB);
+        for (int k = 0; k < 4; ++k) {
+          const int r = 8 * half + 2 * k;  // low half-word: element r, high: r + 1
+          const uint32_t keep = (dead(r) ? 0u : 0x0000FFFFu) | (dead(r + 1) ? 0u : 0xFFFF0000u);
+          pw[k] &= keep;
+          dw[k] &= keep;
+        }
+        pbf[set][half] = __builtin_bit_cast(bf16x8, pw);
+        dsbf[set][half] = __builtin_bit_cast(bf16x8, dw);
       }
     }
   };
-  auto mfma_step = [&](int p, const bf16x8* o) __attribute__((always_inline)) {
-    if (p < 2) {
-#pragma unroll
-      for (int dd = 0; dd < DD; ++dd) {
-        dv[dd] = mfma32(pbf[p], o[2 * dd], dv[dd]);
-        dk[dd] = mfma32(dsbf[p], o[2 * dd + 1], dk[dd]);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < DS / 2; ++j) {
-        const int ds = (DS / 2) * (p - 2) + j;
-        const bool first = ds == 0;
-        s = mfma32(o[2 * j], kreg[ds], first ? f32x16{} : s);
-        dp = mfma32(o[2 * j + 1], vreg[ds], first ? f32x16{} : dp);
-      }
-    }
-  };
-  // Runs steps [p0, p1); the operands of step p0 must already be in ob[p0&1].
-  auto steps = [&](int p0, int p1, const char* pst, int pqs, const char* sst, int sqs)
-      __attribute__((always_inline)) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      if (p >= p0 && p < p1) {
-        if (p + 1 < p1) load_step(p + 1, p + 1 < 2 ? pst : sst, p + 1 < 2 ? pqs : sqs, ob[(p + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);  // keep the next step's reads ahead
-        mfma_step(p, ob[p & 1]);
-      }
-    }
-  };
-  // Multiply sub-tile (t, qs), then score the next sub-tile (tn, 1 - qs).
-  auto full_phase = [&](int t, int qs, int tn) __attribute__((always_inline)) {
-    grad(t, qs);
+  // Step: scores of (t, qs) into set `set`; products of the previous
+  // sub-tile (pt, pqs) from the other set, if `prod`.
+  auto step = [&](int t, int qs, int set, bool prod, int pt, int pqs) __attribute__((always_inline)) {
+    scores(t, qs);
+    MfmaReadPipeline<2 * DS, 1, 0, 0, 4>::apply();
     __builtin_amdgcn_sched_barrier(0);
-    load_step(0, stage_of(t), qs, ob[0]);
-    steps(0, 4, stage_of(t), qs, stage_of(tn), 1 - qs);
+    prod_grad(prod, pt, pqs, 1 - set, true, t, qs, set);
+    mask_grad(t, qs, set);
   };
-  auto score_phase = [&](int tn, int sqs) __attribute__((always_inline)) {
-    load_step(2, stage_of(tn), sqs, ob[0]);
-    steps(2, 4, nullptr, 0, stage_of(tn), sqs);
-  };
-  auto prod_phase = [&](int t, int qs) __attribute__((always_inline)) {
-    grad(t, qs);
-    __builtin_amdgcn_sched_barrier(0);
-    load_step(0, stage_of(t), qs, ob[0]);
-    steps(0, 2, stage_of(t), qs, nullptr, 0);
-  };
-  auto end_tile = [&](int t) __attribute__((always_inline)) {
-    if (t + 1 < ntiles) ld_write(t + 1);
-    // Iteration t+1 reads stage t+2 (issued in iteration t-1); this
+
+  auto end_iter = [&](int t) __attribute__((always_inline)) {
+    // Iteration t+1 reads stage t+1 (issued in iteration t-1); this
     // iteration's loads may stay in flight.
-    if (t + 3 < ntiles)
+    if (t + 2 < ntiles)
       wait_vmem_n<VPT>();
     else
       wait_vmem();
     __syncthreads();
   };
-  auto begin_tile = [&](int t) __attribute__((always_inline)) {
-    if (t + 3 < ntiles) issue(t + 3);
-    if (t + 1 < ntiles) ld_read(t + 1);
-  };
 
-  // Tiles before this wave's first active tile: only keep the pipeline
-  // moving; the last of them scores sub-tile (ft, 0).
+  // Tiles before this wave's first active tile: keep the pipeline moving.
   int t = 0;
   for (; t < min(ft, ntiles); ++t) {
-    begin_tile(t);
-    if (t + 1 == ft && ft < ntiles) score_phase(ft, 0);
-    end_tile(t);
+    if (t + 2 < ntiles) issue(t + 2);
+    end_iter(t);
   }
-  if (ft == 0 && ntiles > 0) score_phase(0, 0);
-  // Steady state: both sub-tiles multiplied, the next two scored.
-  for (; t + 1 < ntiles; ++t) {
-    begin_tile(t);
-    full_phase(t, 0, t);
-    full_phase(t, 1, t + 1);
-    end_tile(t);
+  if (t < ntiles) {  // first active tile: nothing to multiply before it
+    if (t + 2 < ntiles) issue(t + 2);
+    convert_ld(t);
+    step(t, 0, 0, false, 0, 0);
+    step(t, 1, 1, true, t, 0);
+    end_iter(t);
+    ++t;
   }
-  // Last tile: nothing left to score after its second sub-tile.
-  if (t < ntiles) {
-    begin_tile(t);
-    full_phase(t, 0, t);
-    prod_phase(t, 1);
-    end_tile(t);
+  for (; t < ntiles; ++t) {
+    if (t + 2 < ntiles) issue(t + 2);
+    convert_ld(t);
+    step(t, 0, 0, true, t - 1, 1);
+    step(t, 1, 1, true, t, 0);
+    end_iter(t);
   }
+  // The last sub-tile's products (its stage is not reloaded after the loop).
+  if (ft < ntiles) prod_grad(true, ntiles - 1, 1, 1, false, 0, 0, 0);
+  acc_ready(dk, dv);
 
   // dK / dV rows: lane holds head-dim column dd*32 + l32 of keys
   // kw0 + 8*(r/4) + 4*hl + r%4.

@@ -11,8 +11,10 @@ namespace ra {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -26,6 +28,24 @@ constexpr float kNegBig = -1.0e30f;
 // it receives D[8*(r/4) + 4*(l/32) + r%4][l%32] in register r = 0..15.
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// acc += A * B with the accumulator held in AGPRs (inline asm, so that the
+// register allocator keeps it out of the VGPR budget).  The compiler does not
+// see inside the asm, so the asm itself provides the two wait states an MFMA
+// needs after a vector instruction writes one of its A / B registers.
+// Consecutive uses of one accumulator need no wait (exact overlap).
+__device__ __forceinline__ void mfma32_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Before anything else reads accumulators written by mfma32_acc: covers the
+// wait states between the last MFMA writing them and a read (the asm takes
+// each accumulator as an operand, so no read is scheduled above it).
+template <int N>
+__device__ __forceinline__ void acc_ready(f32x16 (&x)[N], f32x16 (&y)[N]) {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+a"(x[i]), "+a"(y[i]));
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
