@@ -327,13 +327,13 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
   };
   // In-place conversion of this wave's copy for tile t (one lse and one
   // delta per lane): lse -> -lse*log2e, where -inf (a row that saw no key)
-  // and rows past the end give P = 0; delta past the end -> 0.
+  // and rows past the end give P = 0; delta -> -delta, 0 past the end.
   auto convert_ld = [&](int t) __attribute__((always_inline)) {
     float* row = &s_ld[t % C::NSTAGE][wave][0][0];
     const bool valid = qstart + t * BQ + lane < Lq;
     const float l = row[lane], d = row[BQ + lane];
     row[lane] = (!valid || l == -INFINITY) ? -INFINITY : -l * kLog2e;
-    row[BQ + lane] = valid ? d : 0.f;
+    row[BQ + lane] = valid ? -d : 0.f;
   };
 
   if (ntiles > 0) issue(0);
@@ -360,89 +360,116 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
   auto stage_of = [&](int t) __attribute__((always_inline)) -> const char* {
     return smem + (t % C::NSTAGE) * C::STAGEB;
   };
-  // S = Q K^T and dP = dO V^T of sub-tile (t, qs).
-  auto scores = [&](int t, int qs) __attribute__((always_inline)) {
-    const char* st = stage_of(t) + qs * 32 * C::ROWB;
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      const bf16x8 aq = *(const bf16x8*)(st + off.row[ds]);
-      const bf16x8 ado = *(const bf16x8*)(st + C::TILEB + off.row[ds]);
-      s = mfma32(aq, kreg[ds], ds == 0 ? f32x16{} : s);
-      dp = mfma32(ado, vreg[ds], ds == 0 ? f32x16{} : dp);
-    }
+  // Operands.  Scores MFMA m of sub-tile (t, qs): m < DS accumulates S over
+  // head-dim slice m (Q rows), DS <= m < 2 DS accumulates dP - delta over
+  // slice m - DS (dO rows, starting from -delta); 16-byte row reads.  Product MFMA i: i = 2*(DD*p + dd) + w, p
+  // the 16-query half, w = 0 the dO^T operand of dV[dd], w = 1 the Q^T
+  // operand of dK[dd]; transpose reads.
+  auto score_operand = [&](int t, int qs, int m) __attribute__((always_inline)) -> bf16x8 {
+    const char* b = stage_of(t) + qs * 32 * C::ROWB + (m >= DS ? C::TILEB : 0);
+    return *(const bf16x8*)(b + off.row[m % DS]);
   };
-  // Operand of product MFMA i of sub-tile (t, qs): i = 2*(DD*p + dd) + w,
-  // p the 16-query half, w = 0 the dO^T operand of dV[dd], w = 1 the Q^T
-  // operand of dK[dd] (transpose reads).
   auto prod_operand = [&](int t, int qs, int i) __attribute__((always_inline)) -> bf16x8 {
     const int p = i / (2 * DD), dd = (i / 2) % DD, w = i & 1;
     const char* b = stage_of(t) + (qs * 32 + 16 * p) * C::ROWB + (w == 0 ? C::TILEB : 0);
     return cat(lds_read_tr((const bf16*)(b + off.tr[dd])),
                lds_read_tr((const bf16*)(b + off.tr[dd] + off.trd)));
   };
-  f32x4 nl[4], dl[4];  // -lse*log2e and delta of the 16 query rows a lane holds
-  // The second half of a step, scheduled by hand in 16 chunks separated by
-  // scheduling barriers: chunk i issues product MFMA i of sub-tile (pt, pqs)
-  // (P / dS from set pset; dV, dK accumulate in AGPRs, see mfma32_acc), the
-  // transpose reads of product MFMA i + LEAD, and the vector work of element
-  // i of the gradient of the newest scores (exp2 of element i, dS and the
-  // bf16 rounding of element i - 1) into set gset.
-  auto prod_grad = [&](bool prod, int pt, int pqs, int pset, bool dograd, int gt, int gqs,
-                       int gset) __attribute__((always_inline)) {
-    constexpr int NP = 2 * 2 * DD, LEAD = 4;
-    if (dograd) {
-      const float* row = &s_ld[gt % C::NSTAGE][wave][0][0];
+  constexpr int NS = 2 * DS, NP = 4 * DD, LEAD = 4;
+  constexpr int EPC = 16 / NP;  // gradient elements per product MFMA
+  static_assert(16 % NP == 0, "gradient chunking");
+  f32x4 nl[4];   // -lse*log2e of the 16 query rows a lane holds
+  f32x16 ndl;    // -delta of the same rows: the dP accumulators start from it
+  bf16x8 sop[LEAD];    // first scores operands of the next step, read ahead
+  // One step, scheduled by hand as NS + NP chunks separated by scheduling
+  // barriers.  Chunk c issues MFMA c of the step (scores of sub-tile (t, qs)
+  // for c < NS, then products of sub-tile (pt, pqs) from P / dS set 1 - set,
+  // accumulating in AGPRs, see mfma32_acc), the operand reads of MFMA c + LEAD
+  // (for the last chunks: the next step's first scores operands, when it reads
+  // the same, already visible, stage), and in the product chunks EPC
+  // elements of the gradient of (t, qs) into set `set`: exp2 as soon as S is
+  // complete, dS and the bf16 rounding two chunks later, once dP is.
+  auto step = [&](int t, int qs, int set, bool prod, int pt, int pqs, bool pre_in,
+                  bool pre_out, int nt, int nqs) __attribute__((always_inline)) {
+    bf16x8 op[NS + NP];
+#pragma unroll
+    for (int i = 0; i < LEAD; ++i) op[i] = pre_in ? sop[i] : score_operand(t, qs, i);
+    {
+      const float* row = &s_ld[t % C::NSTAGE][wave][0][0];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        nl[g] = *(const f32x4*)&row[gqs * 32 + 8 * g + 4 * hl];
-        dl[g] = *(const f32x4*)&row[BQ + gqs * 32 + 8 * g + 4 * hl];
-      }
-    }
-    bf16x8 op[NP];
-    if (prod) {
+        nl[g] = *(const f32x4*)&row[qs * 32 + 8 * g + 4 * hl];
+        const f32x4 d = *(const f32x4*)&row[BQ + qs * 32 + 8 * g + 4 * hl];
 #pragma unroll
-      for (int i = 0; i < LEAD; ++i) op[i] = prod_operand(pt, pqs, i);
+        for (int i = 0; i < 4; ++i) ndl[4 * g + i] = d[i];
+      }
     }
     f32x16 pr, dsr;
     u32x4 pw[2], dw[2];
     auto finish = [&](int r) __attribute__((always_inline)) {  // dS and rounding of element r
-      dsr[r] = pr[r] * (dp[r] - dl[r >> 2][r & 3]);
+      dsr[r] = pr[r] * dp[r];  // dP already holds dO V^T - delta
       if (r & 1) {
         const bf16x2 pp = {(bf16)pr[r - 1], (bf16)pr[r]};
-        const bf16x2 dq2 = {(bf16)dsr[r - 1], (bf16)dsr[r]};
+        const bf16x2 d2 = {(bf16)dsr[r - 1], (bf16)dsr[r]};
         pw[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pp);
-        dw[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, dq2);
+        dw[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, d2);
       }
     };
-    // 16 gradient elements per lane; with fewer product MFMAs (D = 64) a
-    // chunk without an MFMA carries only gradient work.
-    constexpr int NCH = NP > 16 ? NP : 16, PER = NCH / NP;
-    static_assert(NCH == 16 && NCH % NP == 0, "chunking");
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      if (prod && c % PER == 0) {
-        const int i = c / PER;
-        const int p = i / (2 * DD), dd = (i / 2) % DD;
+    for (int c = 0; c < NS + NP; ++c) {
+      if (c < DS) {
+        s = mfma32(op[c], kreg[c], c == 0 ? f32x16{} : s);
+      } else if (c < NS) {
+        dp = mfma32(op[c], vreg[c - DS], c == DS ? ndl : dp);
+      } else if (prod) {
+        const int i = c - NS, p = i / (2 * DD), dd = (i / 2) % DD;
         if ((i & 1) == 0)
-          mfma32_acc(dv[dd], pbf[pset][p], op[i]);
+          mfma32_acc(dv[dd], pbf[1 - set][p], op[c]);
         else
-          mfma32_acc(dk[dd], dsbf[pset][p], op[i]);
-        if (i + LEAD < NP) op[i + LEAD] = prod_operand(pt, pqs, i + LEAD);
+          mfma32_acc(dk[dd], dsbf[1 - set][p], op[c]);
       }
-      if (dograd) {
-        pr[c] = exp2_fast(fmaf(s[c], c2, nl[c >> 2][c & 3]));
-        if (c > 0) finish(c - 1);
+      const int j = c + LEAD;
+      if (j < NS)
+        op[j] = score_operand(t, qs, j);
+      else if (j < NS + NP) {
+        if (prod) op[j] = prod_operand(pt, pqs, j - NS);
+      } else if (pre_out) {
+        sop[j - NS - NP] = score_operand(nt, nqs, j - NS - NP);
+      }
+      if (c >= NS) {
+        const int k = c - NS;
+#pragma unroll
+        for (int e = k * EPC; e < (k + 1) * EPC; ++e) pr[e] = exp2_fast(fmaf(s[e], c2, nl[e >> 2][e & 3]));
+        if (k >= 2) {
+#pragma unroll
+          for (int e = (k - 2) * EPC; e < (k - 1) * EPC; ++e) finish(e);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (dograd) {
-      finish(NCH - 1);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        pbf[gset][h] = __builtin_bit_cast(bf16x8, pw[h]);
-        dsbf[gset][h] = __builtin_bit_cast(bf16x8, dw[h]);
-      }
+    for (int e = 16 - 2 * EPC; e < 16; ++e) finish(e);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      pbf[set][h] = __builtin_bit_cast(bf16x8, pw[h]);
+      dsbf[set][h] = __builtin_bit_cast(bf16x8, dw[h]);
+    }
+  };
+  // Products of the last sub-tile (after the loop; no scores, no gradient).
+  auto last_products = [&](int pt, int pqs, int pset) __attribute__((always_inline)) {
+    bf16x8 op[NP];
+#pragma unroll
+    for (int i = 0; i < LEAD; ++i) op[i] = prod_operand(pt, pqs, i);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int p = i / (2 * DD), dd = (i / 2) % DD;
+      if ((i & 1) == 0)
+        mfma32_acc(dv[dd], pbf[pset][p], op[i]);
+      else
+        mfma32_acc(dk[dd], dsbf[pset][p], op[i]);
+      if (i + LEAD < NP) op[i + LEAD] = prod_operand(pt, pqs, i + LEAD);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   // Keys past the end, or after the query on the diagonal block, take no
@@ -470,16 +497,6 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
       }
     }
   };
-  // Step: scores of (t, qs) into set `set`; products of the previous
-  // sub-tile (pt, pqs) from the other set, if `prod`.
-  auto step = [&](int t, int qs, int set, bool prod, int pt, int pqs) __attribute__((always_inline)) {
-    scores(t, qs);
-    MfmaReadPipeline<2 * DS, 1, 0, 0, 4>::apply();
-    __builtin_amdgcn_sched_barrier(0);
-    prod_grad(prod, pt, pqs, 1 - set, true, t, qs, set);
-    mask_grad(t, qs, set);
-  };
-
   auto end_iter = [&](int t) __attribute__((always_inline)) {
     // Iteration t+1 reads stage t+1 (issued in iteration t-1); this
     // iteration's loads may stay in flight.
@@ -499,20 +516,24 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
   if (t < ntiles) {  // first active tile: nothing to multiply before it
     if (t + 2 < ntiles) issue(t + 2);
     convert_ld(t);
-    step(t, 0, 0, false, 0, 0);
-    step(t, 1, 1, true, t, 0);
+    step(t, 0, 0, false, 0, 0, false, true, t, 1);
+    mask_grad(t, 0, 0);
+    step(t, 1, 1, true, t, 0, true, false, 0, 0);
+    mask_grad(t, 1, 1);
     end_iter(t);
     ++t;
   }
   for (; t < ntiles; ++t) {
     if (t + 2 < ntiles) issue(t + 2);
     convert_ld(t);
-    step(t, 0, 0, true, t - 1, 1);
-    step(t, 1, 1, true, t, 0);
+    step(t, 0, 0, true, t - 1, 1, false, true, t, 1);
+    mask_grad(t, 0, 0);
+    step(t, 1, 1, true, t, 0, true, false, 0, 0);
+    mask_grad(t, 1, 1);
     end_iter(t);
   }
   // The last sub-tile's products (its stage is not reloaded after the loop).
-  if (ft < ntiles) prod_grad(true, ntiles - 1, 1, 1, false, 0, 0, 0);
+  if (ft < ntiles) last_products(ntiles - 1, 1, 1);
   acc_ready(dk, dv);
 
   // dK / dV rows: lane holds head-dim column dd*32 + l32 of keys

@@ -32,11 +32,12 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 // acc += A * B with the accumulator held in AGPRs (inline asm, so that the
 // register allocator keeps it out of the VGPR budget).  The compiler does not
-// see inside the asm, so the asm itself provides the two wait states an MFMA
-// needs after a vector instruction writes one of its A / B registers.
-// Consecutive uses of one accumulator need no wait (exact overlap).
+// see inside the asm: the caller must not write A or B with a vector ALU
+// instruction in the two wait states before (an MFMA reading a VGPR that a
+// VALU op just wrote needs them); LDS loads are covered by the compiler's
+// s_waitcnt.  Consecutive uses of one accumulator need no wait (exact overlap).
 __device__ __forceinline__ void mfma32_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 // Before anything else reads accumulators written by mfma32_acc: covers the
 // wait states between the last MFMA writing them and a read (the asm takes
