@@ -312,32 +312,77 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
   const LdsOffsets<D> off(lane);
   using Loader = TileLoader<D, BQ, NW>;
   const Loader loader(wave, lane);
-  // Per tile each wave issues LPW loads of Q, LPW of dO and its own lse and
-  // delta rows: VPT loads, counted in vmcnt.
-  constexpr int VPT = 2 * Loader::LPW + 2;
-  auto issue = [&](int t) __attribute__((always_inline)) {
-    const int st = t % C::NSTAGE;
-    const int q0t = qstart + t * BQ;
-    loader.issue(smem_lds + st * C::STAGEB, Qp, q0t, Lq);
-    loader.issue(smem_lds + st * C::STAGEB + C::TILEB, dOp, q0t, Lq);
-    const int q = min(q0t + lane, Lq - 1);
-    const uint32_t row = sld_lds + (uint32_t)((st * NW + wave) * 2 * BQ * 4);
-    dma4(Lp + q, row);
-    dma4(Dp + q, row + BQ * 4);
+  // Per iteration t each wave issues VPT copies: LPW of Q and LPW of dO for
+  // tile t+2, and its own lse and delta rows for tile t+3 (they are converted
+  // an iteration before the tile's stage is read).  Copy k < 2 LPW is a Q / dO
+  // copy, 2 LPW and 2 LPW + 1 the lse / delta rows; vmcnt counts them.
+  constexpr int LPW = Loader::LPW;
+  constexpr int VPT = 2 * LPW + 2;
+  auto issue_copy = [&](int t, int k) __attribute__((always_inline)) {
+    if (k < 2 * LPW) {
+      const int tt = t + 2;
+      const uint32_t base = smem_lds + (tt % C::NSTAGE) * C::STAGEB + (k < LPW ? 0 : C::TILEB);
+      dma_tile_loads_split<D, BQ, 1>(base, k < LPW ? Qp : dOp, qstart + tt * BQ, Lq,
+                                     wave * LPW + k % LPW, loader.lane_part);
+    } else {
+      const int tt = t + 3;
+      const int q = min(qstart + tt * BQ + lane, Lq - 1);
+      const uint32_t row = sld_lds + (uint32_t)(((tt % C::NSTAGE) * NW + wave) * 2 * BQ * 4);
+      if (k == 2 * LPW)
+        dma4(Lp + q, row);
+      else
+        dma4(Dp + q, row + BQ * 4);
+    }
   };
+  // Copies of iteration t that exist: Q / dO while t + 2 < ntiles, lse /
+  // delta while t + 3 < ntiles.
+  auto copy_live = [&](int t, int k) __attribute__((always_inline)) -> bool {
+    return k < 2 * LPW ? t + 2 < ntiles : t + 3 < ntiles;
+  };
+  // The same copy when the caller knows it exists and its tile has no rows
+  // past the end: no test, no branch (placed between MFMAs).
+  auto issue_copy_full = [&](int t, int k) __attribute__((always_inline)) {
+    if (k < 2 * LPW) {
+      const int tt = t + 2;
+      const uint32_t base = smem_lds + (tt % C::NSTAGE) * C::STAGEB + (k < LPW ? 0 : C::TILEB);
+      const int j = wave * LPW + k % LPW;
+      const uint32_t voff[1] = {(loader.lane_part ^ dma_xor<D>(j)) + (uint32_t)j * 1024};
+      dma16_group<1>(uniform((k < LPW ? Qp : dOp) + (size_t)(qstart + tt * BQ) * D), voff,
+                     base + (uint32_t)j * 1024);
+    } else {
+      issue_copy(t, k);  // lse / delta rows: clamped, branch-free already
+    }
+  };
+  // Tiles with no rows past the end of the block.
+  const int nfull = qstart < Lq ? (Lq - qstart) / BQ : 0;
   // In-place conversion of this wave's copy for tile t (one lse and one
   // delta per lane): lse -> -lse*log2e, where -inf (a row that saw no key)
   // and rows past the end give P = 0; delta -> -delta, 0 past the end.
-  auto convert_ld = [&](int t) __attribute__((always_inline)) {
+  float ld_l = 0.f, ld_d = 0.f;
+  auto convert_read = [&](int t) __attribute__((always_inline)) {
+    const float* row = &s_ld[t % C::NSTAGE][wave][0][0];
+    ld_l = row[lane];
+    ld_d = row[BQ + lane];
+  };
+  auto convert_write = [&](int t) __attribute__((always_inline)) {
     float* row = &s_ld[t % C::NSTAGE][wave][0][0];
     const bool valid = qstart + t * BQ + lane < Lq;
-    const float l = row[lane], d = row[BQ + lane];
-    row[lane] = (!valid || l == -INFINITY) ? -INFINITY : -l * kLog2e;
-    row[BQ + lane] = valid ? -d : 0.f;
+    row[lane] = (!valid || ld_l == -INFINITY) ? -INFINITY : -ld_l * kLog2e;
+    row[BQ + lane] = valid ? -ld_d : 0.f;
   };
 
-  if (ntiles > 0) issue(0);
-  if (ntiles > 1) issue(1);
+  // Prologue: Q / dO of tiles 0, 1 and lse / delta of tiles 0, 1, 2 (the
+  // copies iterations -2 and -1 would have issued).
+  for (int k = 0; k < VPT; ++k) {
+    if (k < 2 * LPW) {
+      if (copy_live(-2, k)) issue_copy(-2, k);
+      if (copy_live(-1, k)) issue_copy(-1, k);
+    } else {
+      if (copy_live(-3, k)) issue_copy(-3, k);
+      if (copy_live(-2, k)) issue_copy(-2, k);
+      if (copy_live(-1, k)) issue_copy(-1, k);
+    }
+  }
 
   bf16x8 kreg[DS], vreg[DS];
 #pragma unroll
@@ -356,6 +401,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
 
   wait_vmem();
   __syncthreads();
+  if (ntiles > 0) {
+    convert_read(0);
+    convert_write(0);
+  }
 
   auto stage_of = [&](int t) __attribute__((always_inline)) -> const char* {
     return smem + (t % C::NSTAGE) * C::STAGEB;
@@ -378,8 +427,17 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
   constexpr int NS = 2 * DS, NP = 4 * DD, LEAD = 4;
   constexpr int EPC = 16 / NP;  // gradient elements per product MFMA
   static_assert(16 % NP == 0, "gradient chunking");
-  f32x4 nl[4];   // -lse*log2e of the 16 query rows a lane holds
-  f32x16 ndl;    // -delta of the same rows: the dP accumulators start from it
+  // -lse*log2e (nl) and -delta (ndl: the dP accumulators start from it) of
+  // the 16 query rows a lane holds, one set per step of an iteration.
+  f32x4 nl[2][4];
+  f32x16 ndl[2];
+  auto ld_rows = [&](int t, int qs, int g) __attribute__((always_inline)) {  // 1 of 4 read pairs
+    const float* row = &s_ld[t % C::NSTAGE][wave][0][0];
+    nl[qs][g] = *(const f32x4*)&row[qs * 32 + 8 * g + 4 * hl];
+    const f32x4 d = *(const f32x4*)&row[BQ + qs * 32 + 8 * g + 4 * hl];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ndl[qs][4 * g + i] = d[i];
+  };
   bf16x8 sop[LEAD];    // first scores operands of the next step, read ahead
   // One step, scheduled by hand as NS + NP chunks separated by scheduling
   // barriers.  Chunk c issues MFMA c of the step (scores of sub-tile (t, qs)
@@ -389,21 +447,29 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
   // the same, already visible, stage), and in the product chunks EPC
   // elements of the gradient of (t, qs) into set `set`: exp2 as soon as S is
   // complete, dS and the bf16 rounding two chunks later, once dP is.
+  // Side work placed in the chunks of a step (`side`): 1 in step qs = 0 of
+  // iteration t issues the iteration's copies (one per chunk, spread over the
+  // step; only where all of them exist and are full tiles) and reads the lse
+  // / delta rows of step qs = 1; 3 only reads those rows (the copies were
+  // issued before the step); 2 in step qs = 1
+  // converts tile t+1's lse / delta (read early, written later) and then
+  // reads the rows of the next iteration's step qs = 0; 0 does nothing.
+  auto side_work = [&](int side, int t, int c) __attribute__((always_inline)) {
+    constexpr int SPREAD = (NS + NP) / VPT;  // chunks between copies
+    if (side == 1 || side == 3) {
+      if (side == 1 && c % SPREAD == 1 && c / SPREAD < VPT) issue_copy_full(t, c / SPREAD);
+      if (c >= NS + 2 && c < NS + 6) ld_rows(t, 1, c - NS - 2);
+    } else if (side == 2 && t + 1 < ntiles) {
+      if (c == 2) convert_read(t + 1);
+      if (c == NS - 2) convert_write(t + 1);
+      if (c >= NS + 2 && c < NS + 6) ld_rows(t + 1, 0, c - NS - 2);
+    }
+  };
   auto step = [&](int t, int qs, int set, bool prod, int pt, int pqs, bool pre_in,
-                  bool pre_out, int nt, int nqs) __attribute__((always_inline)) {
+                  bool pre_out, int nt, int nqs, int side) __attribute__((always_inline)) {
     bf16x8 op[NS + NP];
 #pragma unroll
     for (int i = 0; i < LEAD; ++i) op[i] = pre_in ? sop[i] : score_operand(t, qs, i);
-    {
-      const float* row = &s_ld[t % C::NSTAGE][wave][0][0];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        nl[g] = *(const f32x4*)&row[qs * 32 + 8 * g + 4 * hl];
-        const f32x4 d = *(const f32x4*)&row[BQ + qs * 32 + 8 * g + 4 * hl];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ndl[4 * g + i] = d[i];
-      }
-    }
     f32x16 pr, dsr;
     u32x4 pw[2], dw[2];
     auto finish = [&](int r) __attribute__((always_inline)) {  // dS and rounding of element r
@@ -421,7 +487,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
       if (c < DS) {
         s = mfma32(op[c], kreg[c], c == 0 ? f32x16{} : s);
       } else if (c < NS) {
-        dp = mfma32(op[c], vreg[c - DS], c == DS ? ndl : dp);
+        dp = mfma32(op[c], vreg[c - DS], c == DS ? ndl[qs] : dp);
       } else if (prod) {
         const int i = c - NS, p = i / (2 * DD), dd = (i / 2) % DD;
         if ((i & 1) == 0)
@@ -440,12 +506,13 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
       if (c >= NS) {
         const int k = c - NS;
 #pragma unroll
-        for (int e = k * EPC; e < (k + 1) * EPC; ++e) pr[e] = exp2_fast(fmaf(s[e], c2, nl[e >> 2][e & 3]));
+        for (int e = k * EPC; e < (k + 1) * EPC; ++e) pr[e] = exp2_fast(fmaf(s[e], c2, nl[qs][e >> 2][e & 3]));
         if (k >= 2) {
 #pragma unroll
           for (int e = (k - 2) * EPC; e < (k - 1) * EPC; ++e) finish(e);
         }
       }
+      side_work(side, t, c);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -498,37 +565,61 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
     }
   };
   auto end_iter = [&](int t) __attribute__((always_inline)) {
-    // Iteration t+1 reads stage t+1 (issued in iteration t-1); this
-    // iteration's loads may stay in flight.
-    if (t + 2 < ntiles)
+    // Iteration t+1 reads stage t+1 and converts tile t+2's lse / delta, both
+    // copied in iteration t-1; this iteration's copies may stay in flight.
+    if (t + 3 < ntiles)
       wait_vmem_n<VPT>();
+    else if (t + 2 < ntiles)
+      wait_vmem_n<2 * LPW>();
     else
       wait_vmem();
     __syncthreads();
   };
 
-  // Tiles before this wave's first active tile: keep the pipeline moving.
+  // Tiles before this wave's first active tile: keep the pipeline moving
+  // (copies, and the conversion of the next tile's lse / delta).
   int t = 0;
   for (; t < min(ft, ntiles); ++t) {
-    if (t + 2 < ntiles) issue(t + 2);
+    for (int k = 0; k < VPT; ++k)
+      if (copy_live(t, k)) issue_copy(t, k);
+    if (t + 1 < ntiles) {
+      convert_read(t + 1);
+      convert_write(t + 1);
+    }
     end_iter(t);
   }
+  auto top_copies = [&](int t) __attribute__((always_inline)) {
+    for (int k = 0; k < VPT; ++k)
+      if (copy_live(t, k)) issue_copy(t, k);
+  };
   if (t < ntiles) {  // first active tile: nothing to multiply before it
-    if (t + 2 < ntiles) issue(t + 2);
-    convert_ld(t);
-    step(t, 0, 0, false, 0, 0, false, true, t, 1);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) ld_rows(t, 0, g);
+    if (t + 3 < nfull) {
+      step(t, 0, 0, false, 0, 0, false, true, t, 1, 1);
+    } else {
+      top_copies(t);
+      step(t, 0, 0, false, 0, 0, false, true, t, 1, 3);
+    }
     mask_grad(t, 0, 0);
-    step(t, 1, 1, true, t, 0, true, false, 0, 0);
+    step(t, 1, 1, true, t, 0, true, false, 0, 0, 2);
     mask_grad(t, 1, 1);
     end_iter(t);
     ++t;
   }
-  for (; t < ntiles; ++t) {
-    if (t + 2 < ntiles) issue(t + 2);
-    convert_ld(t);
-    step(t, 0, 0, true, t - 1, 1, false, true, t, 1);
+  // Steady state: every copy exists and is a full tile.
+  for (; t + 3 < nfull; ++t) {
+    step(t, 0, 0, true, t - 1, 1, false, true, t, 1, 1);
     mask_grad(t, 0, 0);
-    step(t, 1, 1, true, t, 0, true, false, 0, 0);
+    step(t, 1, 1, true, t, 0, true, false, 0, 0, 2);
+    mask_grad(t, 1, 1);
+    end_iter(t);
+  }
+  for (; t < ntiles; ++t) {
+    top_copies(t);
+    step(t, 0, 0, true, t - 1, 1, false, true, t, 1, 3);
+    mask_grad(t, 0, 0);
+    step(t, 1, 1, true, t, 0, true, false, 0, 0, 2);
     mask_grad(t, 1, 1);
     end_iter(t);
   }
