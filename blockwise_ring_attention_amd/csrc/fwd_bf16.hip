@@ -117,6 +117,21 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
   const LdsOffsets<D> off(lane);
 
   const TileLoader<D, BN, NW, true, true> loader(wave, lane);
+  // Branch-free single copies (the caller guarantees that the tile exists
+  // and has no keys past the end).  With eight waves and only full tiles
+  // ahead, each wave issues half of its copies at the top of the iteration
+  // and half between its two phases, which stalls less than a burst of
+  // copies after the barrier.
+  auto copy1 = [&](bool isv, int t, int i) __attribute__((always_inline)) {
+    constexpr int LPW = decltype(loader)::LPW;
+    const uint32_t base = smem_lds + (isv ? C::VBASE : 0) + (t % C::NSLOT) * C::TILEB;
+    const int j = wave * LPW + i;
+    const uint32_t voff[1] = {(loader.lane_part ^ dma_xor<D>(j)) + (uint32_t)j * 1024};
+    dma16_group<1>(uniform((isv ? Vp : Kp) + (size_t)t * BN * D), voff, base + (uint32_t)j * 1024);
+  };
+  const int nfull = Lk / BN;
+  // (every wave issues exactly two copies per tile in this configuration)
+  constexpr bool kSplitCopies = NW == 8 && decltype(loader)::NL == 2 * NW;
   auto issue_k = [&](int t) __attribute__((always_inline)) {
     loader.issue(smem_lds + (t % C::NSLOT) * C::TILEB, Kp, t * BN, Lk);
   };
@@ -232,13 +247,24 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
   for (int t = 0; t < ntiles; ++t) {
     // K slot (t+3)%4 last served iteration t-1 (K tile t-1); V slot
     // (t+2)%4 last served iteration t-1 (V tile t-2).
-    if (t + 3 < ntiles) issue_k(t + 3);
-    if (t + 2 < ntiles) issue_v(t + 2);
+    const bool steady = kSplitCopies && t + 3 < nfull;
+    if (steady) {
+      copy1(false, t + 3, 0);
+      copy1(true, t + 2, 0);
+    } else {
+      if (t + 3 < ntiles) issue_k(t + 3);
+      if (t + 2 < ntiles) issue_v(t + 2);
+    }
     if (!group_b) {
       // A: softmax(t), then value(t) + scores(t+1)
       if (t < ntw) {
         softmax(t);
         __builtin_amdgcn_sched_barrier(0);
+        if (steady) {
+          copy1(false, t + 3, 1);
+          copy1(true, t + 2, 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         __builtin_amdgcn_s_setprio(1);
         value(v_of(t));
         // Unconditional: past the wave's last tile the scores are unused, and
@@ -246,6 +272,9 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
         scores(k_of(t + 1));
         Pipe::apply();
         __builtin_amdgcn_s_setprio(0);
+      } else if (steady) {  // past this wave's last tile: its copies still go out
+        copy1(false, t + 3, 1);
+        copy1(true, t + 2, 1);
       }
     } else {
       // B: value(t-1) + scores(t), then softmax(t)
@@ -261,6 +290,11 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
         __builtin_amdgcn_s_setprio(0);
       }
       __builtin_amdgcn_sched_barrier(0);
+      if (steady) {
+        copy1(false, t + 3, 1);
+        copy1(true, t + 2, 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if (t < ntw) softmax(t);
     }
     // Iteration t+1 reads K tile t+2 and V tile t+1 (issued in iteration
