@@ -19,7 +19,7 @@
 //     with dO^T and Q^T by LDS transpose reads.  Four waves, one per SIMD;
 //     each wave overlaps the products of tile t with the scores of t+1.
 // Tiles move global -> LDS with direct-to-LDS copies into XOR-swizzled rows
-// (see ra_common.h), four stages deep, one tile of prefetch.
+// (see ra_common.h); each kernel keeps two tiles of prefetch in flight.
 // The causal diagonal block masks key j > query i; past blocks are dense.
 #include <math.h>
 
@@ -263,11 +263,13 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
 // other).
 //
 // Memory pipeline: four LDS stages of (Q tile, dO tile).  Iteration t (steps
-// 2t, 2t+1) reads stages t-1 (products(2t-1)) and t, issues tile t+2 into the
-// slot of tile t-2, and at its end waits for tile t+1 only.  Each wave keeps
-// a private copy of the tile's lse / delta rows (two 4-byte direct-to-LDS
-// copies) and converts it in place at the start of the iteration that uses
-// it, so no extra barrier is needed.
+// 2t, 2t+1) reads stages t-1 (products(2t-1)) and t, copies tile t+2 into
+// the slot of tile t-2, and at its end waits for tile t+1 only.  Each wave
+// keeps a private copy of the tile's lse / delta rows (two 4-byte
+// direct-to-LDS copies, issued for tile t+3) and converts it in place one
+// iteration before the tile is used, so no extra barrier is needed.  Where
+// every tile ahead is full, the copies and the conversion are placed between
+// the MFMAs of the steps instead of in a burst after the barrier.
 template <int D, int BQ, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ KV,

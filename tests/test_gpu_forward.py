@@ -51,6 +51,7 @@ SMALL = [
     ("bf16 d64 causal", "bf16", 1, 3, 64, 4, 160, 3, True, 256, 64),
     ("bf16 d64 noncausal", "bf16", 1, 2, 64, 3, 96, 0, False, 128, 32),
     ("bf16 d128 noncausal rank1", "bf16", 2, 2, 128, 4, 130, 1, False, 256, 64),
+    ("bf16 d128 diagonal only, three workgroups", "bf16", 1, 2, 128, 2, 600, 0, True, 256, 64),
     ("fp32 d128 causal ragged", "fp32", 1, 2, 128, 3, 100, 2, True, 64, 64),
     ("fp32 d64 noncausal", "fp32", 1, 2, 64, 2, 77, 1, False, 64, 64),
 ]
