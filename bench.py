@@ -52,7 +52,41 @@ def _parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (a known amount of "
                          "HBM traffic, to scale the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--trace-overlap", metavar="KERNEL_TRACE_CSV",
+                    help="no GPU: read a rocprofv3 --kernel-trace CSV of this benchmark and "
+                         "report how much of the ring-hop copy time overlaps the attention "
+                         "kernels, then exit")
     return ap.parse_args()
+
+
+# Kernel-name fragments of the attention kernels and of the emulated ring
+# hop (hipMemcpyAsync device-to-device copies run as copy kernels).
+_ATTN_KERNELS = ("fwd_bf16_kernel", "fwd_fp32_kernel", "dq_kernel", "dkv_kernel")
+_COPY_KERNEL = "copyBuffer"
+
+
+def _trace_overlap(path):
+    """Fraction of copy-kernel time during which an attention kernel runs."""
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    span = lambda r: (int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+    attn = sorted(span(r) for r in rows if any(k in r["Kernel_Name"] for k in _ATTN_KERNELS))
+    copies = [r for r in rows if _COPY_KERNEL in r["Kernel_Name"]]
+    total = covered = 0
+    for r in copies:
+        a, b = span(r)
+        total += b - a
+        # attention kernels run one at a time on the main stream: no double count
+        covered += sum(min(b, e) - max(a, s) for s, e in attn if s < b and e > a)
+    print(json.dumps({
+        "copy_kernels": len(copies),
+        "copy_ms": round(total / 1e6, 3),
+        "copy_ms_overlapped_by_attention": round(covered / 1e6, 3),
+        "overlap_fraction": round(covered / total, 4) if total else None,
+        "copy_queues": sorted({r["Queue_Id"] for r in copies}),
+        "attention_queues": sorted({r["Queue_Id"] for r in rows
+                                    if any(k in r["Kernel_Name"] for k in _ATTN_KERNELS)}),
+    }))
 
 
 def _copy_calibration():
@@ -146,6 +180,9 @@ def _cpu_baseline(host, cfg, rank, target_s):
 
 def main():
     args = _parse()
+    if args.trace_overlap:
+        _trace_overlap(args.trace_overlap)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one ring member's share on one GPU; --gpus {args.gpus} "

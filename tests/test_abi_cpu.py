@@ -114,3 +114,25 @@ def test_emulator_rejects_bad_schedules(lib):
                           ctypes.c_void_p(0x10000000), ctypes.c_void_p(0x20000000),
                           ctypes.byref(d), None, 0, None, None)
     assert rc == -1 and b"slot" in lib.ring_attn_last_error()
+
+
+def test_bench_trace_overlap_report(tmp_path, capsys):
+    """The copy/compute overlap report of bench.py on a hand-made trace."""
+    import json
+    import bench
+    path = tmp_path / "trace.csv"
+    cols = ["Queue_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+    rows = [("1", "void fwd_bf16_kernel<128, 64, 8>(...)", 100, 200),
+            ("1", "void dq_kernel<128, 64, 8>(...)", 200, 300),
+            ("2", "__amd_rocclr_copyBuffer", 150, 250),   # fully under attention
+            ("2", "__amd_rocclr_copyBuffer", 280, 380)]   # 20 of 100 under attention
+    import csv
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f, quoting=csv.QUOTE_NONNUMERIC)
+        w.writerow(cols)
+        w.writerows(rows)
+    bench._trace_overlap(str(path))
+    out = json.loads(capsys.readouterr().out)
+    assert out["copy_kernels"] == 2
+    assert out["overlap_fraction"] == round(120 / 200, 4)
+    assert out["copy_queues"] == ["2"] and out["attention_queues"] == ["1"]
