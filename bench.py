@@ -110,10 +110,10 @@ KERNEL_SOURCES = {
 COMMON_SOURCE = "blockwise_ring_attention_amd/csrc/ra_common.h"
 
 
-def _measured_traffic(family):
-    """HBM bytes per launch of a kernel family from the committed FETCH_SIZE /
-    WRITE_SIZE counter runs (scaled by the copy calibration), or None when the
-    kernel's source has changed since the counters were taken."""
+def _profiled(family):
+    """The committed counter record of a kernel family (and the file's
+    calibration factors), or None when the kernel's source has changed since
+    the counters were taken."""
     import hashlib
     try:
         with open(TRAFFIC_FILE) as f:
@@ -125,11 +125,28 @@ def _measured_traffic(family):
                 h.update(f.read())
         if h.hexdigest()[:16] != k["source_sha256_16"]:
             return None
-        kib = k["fetch_kib_per_dispatch"] * rec["fetch_factor"] + \
-            k["write_kib_per_dispatch"] * rec["write_factor"]
-        return int(kib * 1024)
+        return rec, k
     except (OSError, KeyError, ValueError):
         return None
+
+
+def _measured_traffic(family):
+    """HBM bytes per launch of a kernel family from the committed FETCH_SIZE /
+    WRITE_SIZE counter runs (scaled by the copy calibration), or None."""
+    p = _profiled(family)
+    if p is None:
+        return None
+    rec, k = p
+    kib = k["fetch_kib_per_dispatch"] * rec["fetch_factor"] + \
+        k["write_kib_per_dispatch"] * rec["write_factor"]
+    return int(kib * 1024)
+
+
+def _measured_mfma_util(family):
+    """MFMA busy percentage of a past-block launch (rocprofv3's MfmaUtil:
+    SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs), or None."""
+    p = _profiled(family)
+    return None if p is None else p[1].get("mfma_util_pct")
 
 
 def _cpu_baseline(host, cfg, rank, target_s):
@@ -272,11 +289,13 @@ def main():
         per_kernel[fam] = {"launches": rec["launches"], "avg_ms": round(avg_ms, 4),
                            "total_ms_per_step": round(rec["total_ms"] / args.steps, 3),
                            "tflops": round(achieved, 1),
-                           "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+                           "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                           "mfma_busy_pct_counter": _measured_mfma_util(fam)}
     dom = max(per_kernel, key=lambda f: per_kernel[f]["total_ms_per_step"])
     roofline = {"bound": "mfma", "achieved": per_kernel[dom]["tflops"], "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": per_kernel[dom]["frac"],
                 "traffic": _measured_traffic(dom), "traffic_unit": "HBM bytes per launch",
+                "mfma_busy_pct_counter": _measured_mfma_util(dom),
                 "kernel": dom}
 
     result = {
