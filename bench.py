@@ -239,24 +239,28 @@ def main():
         fwd()
         bwd()
 
-    def timed(fn, steps):
+    def timed(fn, steps, per_step=None):
+        """Mean ms per step between two events around all steps (and, if
+        per_step is a list, each step's own ms appended to it)."""
         torch.cuda.synchronize()
-        start = torch.cuda.Event(enable_timing=True)
-        stop = torch.cuda.Event(enable_timing=True)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         w0 = time.perf_counter()
-        start.record(main_stream)
-        for _ in range(steps):
+        ev[0].record(main_stream)
+        for i in range(steps):
             fn()
-        stop.record(main_stream)
+            ev[i + 1].record(main_stream)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - w0) * 1e3 / steps
-        return start.elapsed_time(stop) / steps, wall
+        if per_step is not None:
+            per_step.extend(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+        return ev[0].elapsed_time(ev[steps]) / steps, wall
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     _lib.ring_attn_timing_enable(True)
-    ms_step, wall_step = timed(step, args.steps)
+    step_ms = []
+    ms_step, wall_step = timed(step, args.steps, step_ms)
     _lib.ring_attn_timing_enable(False)
     kernels = {}
     for fam in ("fwd_bf16", "bwd_dq", "bwd_dkv"):
@@ -320,6 +324,8 @@ def main():
                    "unmasked_pairs": pairs},
         "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "wall_ms_per_step": round(wall_step, 3),
+        "step_ms_median": round(sorted(step_ms)[len(step_ms) // 2], 3),
+        "step_ms_min": round(min(step_ms), 3),
         "phases": phases,
         "kernels": per_kernel,
         "roofline": roofline,
