@@ -188,7 +188,14 @@ def _cpu_baseline(host, cfg, rank, target_s):
         heads = int(min(cfg.heads, max(1, round(target_s / max(dt, 1e-3)))))
         dt, pairs = run(list(range(heads)), nrows)
     flops = (FWD_FLOPS_PER_PAIR_PER_D + BWD_FLOPS_PER_PAIR_PER_D) * cfg.head_dim * pairs
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model,
             "sample": (f"fp64 oracle forward + gradients for the last {nrows} query rows of "
                        f"{heads} head(s) against all {len(k_pos)} keys ({pairs} unmasked pairs), "
                        f"{dt:.1f} s"),
