@@ -119,3 +119,22 @@ def test_cfg4_full_size():
             check(f"dk[{kb}] h{h}", dev.dkv_pool[kb][0][:, [h]], dk_ref, "bf16")
             check(f"dv[{kb}] h{h}", dev.dkv_pool[kb][1][:, [h]], dv_ref, "bf16")
     assert torch.isfinite(dev.dq_acc).all()
+
+
+def test_causal_independence_bitwise():
+    """Keys after position p (values too) never reach the rows at or before p:
+    perturbing them leaves those rows of o, lse and dQ bitwise unchanged
+    (the exact causal mask across seams; darcstar commentary)."""
+    cfg = ShareConfig(96, "indep", "bf16", 1, 2, 128, 2, 300, (1,), True, 256, 64,
+                      backward=True)
+    host = share.make_host_share(cfg, 1, seed=11, backward=True)
+    p = 137  # local position inside the diagonal block (a ragged, mid-tile row)
+    g = torch.Generator().manual_seed(5)
+    kv = host.kv[1].clone()
+    kv[:, :, :, p + 1:] = (torch.randn(kv[:, :, :, p + 1:].shape, generator=g) * 2).to(kv.dtype)
+    other = share.HostShare(cfg, 1, host.q, {0: host.kv[0], 1: kv}, host.dout)
+    a, b = _run(host), _run(other)
+    assert not torch.equal(a.o_acc[:, :, p + 1:], b.o_acc[:, :, p + 1:])  # the change matters
+    assert torch.equal(a.o_acc[:, :, :p + 1], b.o_acc[:, :, :p + 1])
+    assert torch.equal(a.lse_acc[:, :, :p + 1], b.lse_acc[:, :, :p + 1])
+    assert torch.equal(a.dq_acc[:, :, :p + 1], b.dq_acc[:, :, :p + 1])
