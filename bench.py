@@ -52,6 +52,9 @@ def _parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (a known amount of "
                          "HBM traffic, to scale the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--kv-heads", type=int, default=0,
+                    help="key/value heads shared by groups of the 32 query heads (MQA / GQA); "
+                         "0 (default): 32, ordinary multi-head attention")
     ap.add_argument("--trace-overlap", metavar="KERNEL_TRACE_CSV",
                     help="no GPU: read a rocprofv3 --kernel-trace CSV of this benchmark and "
                          "report how much of the ring-hop copy time overlaps the attention "
@@ -173,8 +176,9 @@ def _cpu_baseline(host, cfg, rank, target_s):
         pairs = 0
         t0 = time.perf_counter()
         for h in heads:
-            k = torch.cat([host.kv[b][0][:, h:h + 1] for b in blocks], dim=2)
-            v = torch.cat([host.kv[b][1][:, h:h + 1] for b in blocks], dim=2)
+            kh = oracle.exact._kv_head(h, cfg.heads, cfg.n_kv_heads)
+            k = torch.cat([host.kv[b][0][:, kh:kh + 1] for b in blocks], dim=2)
+            v = torch.cat([host.kv[b][1][:, kh:kh + 1] for b in blocks], dim=2)
             q = host.q[:, h:h + 1, rows]
             do = host.dout[:, h:h + 1, rows]
             oracle.attention_grads(q, k, v, do, q_pos, k_pos, cfg.causal)
@@ -225,7 +229,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     _lib.load()
-    cfg = scaled(CONFIGS[3], backward=True)
+    cfg = scaled(CONFIGS[3], backward=True, kv_heads=args.kv_heads)
+    mha = cfg.n_kv_heads == cfg.heads
     rank = cfg.ranks[0]
     t_gen = time.perf_counter()
     host = share.make_host_share(cfg, rank, seed=0, backward=True)
@@ -301,12 +306,14 @@ def main():
                            "total_ms_per_step": round(rec["total_ms"] / args.steps, 3),
                            "tflops": round(achieved, 1),
                            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                           "mfma_busy_pct_counter": _measured_mfma_util(fam)}
+                           "mfma_busy_pct_counter": _measured_mfma_util(fam) if mha else None}
     dom = max(per_kernel, key=lambda f: per_kernel[f]["total_ms_per_step"])
     roofline = {"bound": "mfma", "achieved": per_kernel[dom]["tflops"], "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": per_kernel[dom]["frac"],
-                "traffic": _measured_traffic(dom), "traffic_unit": "HBM bytes per launch",
-                "mfma_busy_pct_counter": _measured_mfma_util(dom),
+                # the committed counters were taken on the multi-head workload
+                "traffic": _measured_traffic(dom) if mha else None,
+                "traffic_unit": "HBM bytes per launch",
+                "mfma_busy_pct_counter": _measured_mfma_util(dom) if mha else None,
                 "kernel": dom}
 
     result = {
@@ -323,8 +330,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": ("lwm7b-causal-ring-share fwd+bwd: batch 1, 32 heads, head_dim 128, "
-                                "ring 8, rank 7, 16384 local queries x 131072 keys"),
-                   "batch": cfg.batch, "heads": cfg.heads, "head_dim": d,
+                                "ring 8, rank 7, 16384 local queries x 131072 keys"
+                                + (f", {cfg.n_kv_heads} shared key/value heads"
+                                   if cfg.n_kv_heads != cfg.heads else "")),
+                   "batch": cfg.batch, "heads": cfg.heads, "kv_heads": cfg.n_kv_heads,
+                   "head_dim": d,
                    "ring_size": cfg.ring_size, "rank": rank, "local_queries": cfg.block_len,
                    "keys": cfg.block_len * (rank + 1), "causal": cfg.causal,
                    "q_chunk": cfg.q_chunk, "k_chunk": cfg.k_chunk,

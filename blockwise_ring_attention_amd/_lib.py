@@ -34,7 +34,7 @@ class Dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
                 ("q_len", ctypes.c_int32), ("kv_len", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("scale", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("kv_heads", ctypes.c_int32)]
 
 
 _lib = None
@@ -120,10 +120,11 @@ def _need(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
 
 
-def dims(q: torch.Tensor, kv_len: int, scale: float = 0.0) -> Dims:
-    """Dims of a call from the query tensor [B, H, Lq, d] and the block length."""
+def dims(q: torch.Tensor, kv_len: int, scale: float = 0.0, kv_heads: int = 0) -> Dims:
+    """Dims of a call from the query tensor [B, H, Lq, d], the block length
+    and the number of key/value heads (0: one per query head)."""
     B, H, Lq, d = q.shape
-    return Dims(B, H, Lq, kv_len, d, _dtype_code(q), float(scale))
+    return Dims(B, H, Lq, kv_len, d, _dtype_code(q), float(scale), int(kv_heads))
 
 
 def ring_attn_init_acc(o_acc, lse_acc, scale=0.0, stream=None):
@@ -139,7 +140,7 @@ def ring_attn_fwd(q, kv_block, ring_rank, ring_step, ring_size, causal, q_chunk,
     _need(kv_block, q.dtype, "kv_block")
     _need(o_acc, torch.float32, "o_acc")
     _need(lse_acc, torch.float32, "lse_acc")
-    dm = dims(q, kv_block.shape[3], scale)
+    dm = dims(q, kv_block.shape[3], scale, kv_block.shape[2])
     _check(load().ring_attn_fwd(_ptr(q), _ptr(kv_block), ring_rank, ring_step, ring_size,
                                 int(bool(causal)), q_chunk, k_chunk, _ptr(o_acc), _ptr(lse_acc),
                                 ctypes.byref(dm), _stream(stream)))
@@ -176,7 +177,7 @@ def ring_attn_bwd(q, kv_block, dout, lse, delta, ring_rank, ring_step, ring_size
     _need(dout, q.dtype, "dout")
     for t, n in ((lse, "lse"), (delta, "delta"), (dq_acc, "dq_acc"), (dkv_io, "dkv_io")):
         _need(t, torch.float32, n)
-    dm = dims(q, kv_block.shape[3], scale)
+    dm = dims(q, kv_block.shape[3], scale, kv_block.shape[2])
     _check(load().ring_attn_bwd(_ptr(q), _ptr(kv_block), _ptr(dout), _ptr(lse), _ptr(delta),
                                 ring_rank, ring_step, ring_size, int(bool(causal)), q_chunk,
                                 k_chunk, _ptr(dq_acc), _ptr(dkv_io), ctypes.byref(dm),
@@ -205,7 +206,7 @@ def ring_emu_fwd(q, kv_pool, slots, ring_rank, ring_size, causal, q_chunk, k_chu
     if len(kv_pool) != ring_size:
         raise ValueError("kv_pool must have ring_size entries")
     ref = next(t for t in kv_pool if t is not None)
-    dm = dims(q, ref.shape[3], scale)
+    dm = dims(q, ref.shape[3], scale, ref.shape[2])
     main = main_stream if main_stream is not None else torch.cuda.current_stream()
     side = side_stream if side_stream is not None else main
     _check(load().ring_emu_fwd(_ptr(q), _ptr_array(kv_pool), _ptr(slots[0]), _ptr(slots[1]),
@@ -221,7 +222,7 @@ def ring_emu_bwd(q, kv_pool, slots, dout, lse, delta, dkv_pool, dkv_slots, ring_
     if len(kv_pool) != ring_size or len(dkv_pool) != ring_size:
         raise ValueError("pools must have ring_size entries")
     ref = next(t for t in kv_pool if t is not None)
-    dm = dims(q, ref.shape[3], scale)
+    dm = dims(q, ref.shape[3], scale, ref.shape[2])
     main = main_stream if main_stream is not None else torch.cuda.current_stream()
     side = side_stream if side_stream is not None else main
     _check(load().ring_emu_bwd(_ptr(q), _ptr_array(kv_pool), _ptr(slots[0]), _ptr(slots[1]),

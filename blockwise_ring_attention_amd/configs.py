@@ -38,6 +38,11 @@ class ShareConfig:
     k_chunk: int
     dists: Dict[str, Dist] = field(default_factory=dict)
     backward: bool = False
+    kv_heads: int = 0           # key/value heads shared by groups of query heads; 0: heads
+
+    @property
+    def n_kv_heads(self) -> int:
+        return self.kv_heads or self.heads
 
     def dist(self, tensor: str) -> Dist:
         return self.dists.get(tensor, Dist())

@@ -109,8 +109,13 @@ int ra_check_dims(const ra_dims* d, ra_shape* s) {
     return ra_fail(RA_ERR_UNSUPPORTED, "dtype %d not supported", d->dtype);
   if (!isfinite(d->scale) || d->scale < 0.f)
     return ra_fail(RA_ERR_INVALID, "scale must be finite and positive (0 = default)");
+  const int hkv = d->kv_heads != 0 ? d->kv_heads : d->heads;
+  if (hkv < 0 || (d->heads > 0 && (hkv == 0 || d->heads % hkv != 0)))
+    return ra_fail(RA_ERR_INVALID, "kv_heads %d must divide heads %d (0 = heads)",
+                   d->kv_heads, d->heads);
   s->B = d->batch;
   s->H = d->heads;
+  s->Hkv = hkv;
   s->Lq = d->q_len;
   s->Lk = d->kv_len;
   s->D = d->head_dim;
@@ -119,7 +124,7 @@ int ra_check_dims(const ra_dims* d, ra_shape* s) {
   s->scale = d->scale != 0.f ? d->scale : 1.0f / sqrtf((float)d->head_dim);
   s->bh = (int64_t)s->B * s->H;
   s->q_rows = s->bh * s->Lq;
-  s->kv_rows = s->bh * s->Lk;
+  s->kv_rows = (int64_t)s->B * s->Hkv * s->Lk;
   // every row index handled by a kernel must fit a 32-bit grid
   if (s->q_rows > (int64_t)1 << 40 || s->kv_rows > (int64_t)1 << 40 ||
       (s->bh > 0 && (s->Lq > (1 << 30) || s->Lk > (1 << 30))))
@@ -155,7 +160,7 @@ int ra_fwd_block(const void* q, const void* kv, int kb, int rank, int causal,
                  const ra_shape& s, hipStream_t stream) {
   if (s.q_rows == 0 || s.Lk == 0) return RA_OK;  // empty block: identity
   if (causal && kb > rank) return RA_OK;         // entirely in the future
-  ra_launch L{s.B, s.H, s.Lq, s.Lk, s.D, s.scale, causal && kb == rank ? 1 : 0,
+  ra_launch L{s.B, s.H, s.Lq, s.Lk, s.D, s.Hkv, s.scale, causal && kb == rank ? 1 : 0,
               q_chunk, k_chunk, stream};
   Timed t(s.dtype == RA_BF16 ? kFwdBf16 : kFwdFp32, stream);
   hipError_t e = s.dtype == RA_BF16
@@ -171,7 +176,7 @@ int ra_bwd_block(const void* q, const void* kv, const void* dout, const float* l
                  hipStream_t stream) {
   if (s.q_rows == 0 || s.Lk == 0) return RA_OK;
   if (causal && kb > rank) return RA_OK;
-  ra_launch L{s.B, s.H, s.Lq, s.Lk, s.D, s.scale, causal && kb == rank ? 1 : 0,
+  ra_launch L{s.B, s.H, s.Lq, s.Lk, s.D, s.Hkv, s.scale, causal && kb == rank ? 1 : 0,
               q_chunk, k_chunk, stream};
   Timed tq(kBwdDq, stream);
   hipError_t e = ra_launch_bwd_dq(q, kv, dout, lse, delta, dq_acc, L);
@@ -222,7 +227,7 @@ int ra_check_bwd_buffers(const void* q, const void* kv, const void* dout,
 
 extern "C" {
 
-int ring_attn_version(void) { return 100; }
+int ring_attn_version(void) { return 200; }
 
 int ring_attn_timing_enable(int on) {
   std::lock_guard<std::mutex> g(g_tmu);

@@ -46,7 +46,7 @@ template <int D, int BN, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ KV,
     const bf16* __restrict__ dO, const float* __restrict__ LSE,
-    const float* __restrict__ Delta, float* __restrict__ dQacc, int BH, int Lq,
+    const float* __restrict__ Delta, float* __restrict__ dQacc, int BH, int H, int G, int Lq,
     int Lk, int n_qt, int diag, float c2, float scale) {
   using C = TileCfg<D, BN, NW>;
   constexpr int BM = NW * 32;
@@ -70,10 +70,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
   const int qw0 = q0 + rblk * 32;
   const int qi = qw0 + l32;
 
+  // Groups of G query heads share one key/value head.
+  const int kvbh = (bh / H) * (H / G) + (bh % H) / G;
   const bf16* Qp = Q + (size_t)bh * Lq * D;
   const bf16* dOp = dO + (size_t)bh * Lq * D;
-  const bf16* Kp = KV + (size_t)bh * Lk * D;
-  const bf16* Vp = KV + ((size_t)BH + bh) * Lk * D;
+  const bf16* Kp = KV + (size_t)kvbh * Lk * D;
+  const bf16* Vp = KV + ((size_t)(BH / G) + kvbh) * Lk * D;
 
   const int kend = diag ? min(Lk, q0 + BM) : Lk;
   const int ntiles = (kend + BN - 1) / BN;
@@ -274,7 +276,7 @@ template <int D, int BQ, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ KV,
     const bf16* __restrict__ dO, const float* __restrict__ LSE,
-    const float* __restrict__ Delta, float* __restrict__ dKV, int BH, int Lq,
+    const float* __restrict__ Delta, float* __restrict__ dKV, int BH, int H, int G, int qj, int Lq,
     int Lk, int n_kt, int diag, float c2, float scale) {
   using C = TileCfg<D, BQ, NW>;
   constexpr int BK = NW * 32;  // keys per workgroup
@@ -290,15 +292,18 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: loop bounds derive from it
   const int l32 = lane & 31, hl = lane >> 5;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = tile / n_kt;
+  // This workgroup's key/value head, and the query head of its group that
+  // this launch handles (one launch per member qj of a group of G).
+  const int kvbh = tile / n_kt;
+  const int bh = (kvbh / (H / G)) * H + (kvbh % (H / G)) * G + qj;
   const int k0 = (tile % n_kt) * BK;  // small k0 first: the most causal work
   const int kw0 = k0 + wave * 32;
   const int kj = kw0 + l32;
 
   const bf16* Qp = Q + (size_t)bh * Lq * D;
   const bf16* dOp = dO + (size_t)bh * Lq * D;
-  const bf16* Kp = KV + (size_t)bh * Lk * D;
-  const bf16* Vp = KV + ((size_t)BH + bh) * Lk * D;
+  const bf16* Kp = KV + (size_t)kvbh * Lk * D;
+  const bf16* Vp = KV + ((size_t)(BH / G) + kvbh) * Lk * D;
   const float* Lp = LSE + (size_t)bh * Lq;
   const float* Dp = Delta + (size_t)bh * Lq;
 
@@ -631,8 +636,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
 
   // dK / dV rows: lane holds head-dim column dd*32 + l32 of keys
   // kw0 + 8*(r/4) + 4*hl + r%4.
-  float* dKp = dKV + (size_t)bh * Lk * D;
-  float* dVp = dKV + ((size_t)BH + bh) * Lk * D;
+  float* dKp = dKV + (size_t)kvbh * Lk * D;
+  float* dVp = dKV + ((size_t)(BH / G) + kvbh) * Lk * D;
 #pragma unroll
   for (int dd = 0; dd < DD; ++dd) {
     // all loads of this head-dim tile first, then the stores
@@ -660,6 +665,9 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
 
 // BN = 64 keys per dQ tile with eight waves (256 query rows per workgroup);
 // BQ = 64 queries per dK/dV tile with four waves (128 keys per workgroup).
+// With G query heads per key/value head, the dK/dV kernel runs once per
+// member of a group, each launch adding that query head's contribution
+// (deterministic, in a fixed order).
 hipError_t ra_launch_bwd_dq(const void* q, const void* kv, const void* dout,
                             const float* lse, const float* delta, float* dq_acc,
                             const ra_launch& a) {
@@ -671,7 +679,7 @@ hipError_t ra_launch_bwd_dq(const void* q, const void* kv, const void* dout,
 #define RA_DQ(DD)                                                                         \
   hipLaunchKernelGGL((dq_kernel<DD, 64, NW>), dim3(n_qt * BH), dim3(NW * 64), 0, a.stream, \
                      (const bf16*)q, (const bf16*)kv, (const bf16*)dout, lse, delta, dq_acc, \
-                     BH, a.Lq, a.Lk, n_qt, a.diag, c2, a.scale)
+                     BH, a.H, a.H / a.Hkv, a.Lq, a.Lk, n_qt, a.diag, c2, a.scale)
   if (a.D == 128) RA_DQ(128);
   else if (a.D == 64) RA_DQ(64);
   else return hipErrorInvalidValue;
@@ -683,17 +691,21 @@ hipError_t ra_launch_bwd_dkv(const void* q, const void* kv, const void* dout,
                              const float* lse, const float* delta, float* dkv,
                              const ra_launch& a) {
   constexpr int NW = 4, BK = NW * 32;
-  const int BH = a.B * a.H;
+  const int BH = a.B * a.H, G = a.H / a.Hkv, BHkv = a.B * a.Hkv;
   const int n_kt = (a.Lk + BK - 1) / BK;
-  if ((long long)n_kt * BH <= 0) return hipSuccess;
+  if ((long long)n_kt * BHkv <= 0) return hipSuccess;
   const float c2 = a.scale * kLog2e;
-#define RA_DKV(DD)                                                                          \
-  hipLaunchKernelGGL((dkv_kernel<DD, 64, NW>), dim3(n_kt * BH), dim3(NW * 64), 0, a.stream, \
-                     (const bf16*)q, (const bf16*)kv, (const bf16*)dout, lse, delta, dkv, BH, \
-                     a.Lq, a.Lk, n_kt, a.diag, c2, a.scale)
-  if (a.D == 128) RA_DKV(128);
-  else if (a.D == 64) RA_DKV(64);
-  else return hipErrorInvalidValue;
+  if (a.D != 128 && a.D != 64) return hipErrorInvalidValue;
+  for (int qj = 0; qj < G; ++qj) {
+#define RA_DKV(DD)                                                                            \
+  hipLaunchKernelGGL((dkv_kernel<DD, 64, NW>), dim3(n_kt * BHkv), dim3(NW * 64), 0, a.stream, \
+                     (const bf16*)q, (const bf16*)kv, (const bf16*)dout, lse, delta, dkv, BH,   \
+                     a.H, G, qj, a.Lq, a.Lk, n_kt, a.diag, c2, a.scale)
+    if (a.D == 128) RA_DKV(128);
+    else RA_DKV(64);
 #undef RA_DKV
-  return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }

@@ -79,7 +79,7 @@ struct FwdCfg {
 template <int D, int BN, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ KV,
-    float* __restrict__ Oacc, float* __restrict__ LSEacc, int BH, int Lq,
+    float* __restrict__ Oacc, float* __restrict__ LSEacc, int BH, int H, int G, int Lq,
     int Lk, int n_qt, int diag, float c2) {
   using C = FwdCfg<D, BN, NW>;
   constexpr int KK = BN / 32;  // 32-key sub-tiles per tile
@@ -103,9 +103,11 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
   const int qw0 = q0 + rblk * 32;
   const int qi = qw0 + l32;
 
+  // Groups of G query heads share one key/value head.
+  const int kvbh = (bh / H) * (H / G) + (bh % H) / G;
   const bf16* Qp = Q + (size_t)bh * Lq * D;
-  const bf16* Kp = KV + (size_t)bh * Lk * D;
-  const bf16* Vp = KV + ((size_t)BH + bh) * Lk * D;
+  const bf16* Kp = KV + (size_t)kvbh * Lk * D;
+  const bf16* Vp = KV + ((size_t)(BH / G) + kvbh) * Lk * D;
 
   const int kend = diag ? min(Lk, q0 + C::BM) : Lk;
   const int ntiles = (kend + BN - 1) / BN;
@@ -360,8 +362,8 @@ hipError_t launch(const void* q, const void* kv, float* o_acc, float* lse_acc,
   if (grid <= 0) return hipSuccess;
   const float c2 = a.scale * kLog2e;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, NW>), dim3((unsigned)grid), dim3(C::NT), 0,
-                     a.stream, (const bf16*)q, (const bf16*)kv, o_acc, lse_acc, BH, a.Lq,
-                     a.Lk, n_qt, a.diag, c2);
+                     a.stream, (const bf16*)q, (const bf16*)kv, o_acc, lse_acc, BH, a.H,
+                     a.H / a.Hkv, a.Lq, a.Lk, n_qt, a.diag, c2);
   return hipGetLastError();
 }
 

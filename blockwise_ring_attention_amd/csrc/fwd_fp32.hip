@@ -20,7 +20,7 @@ constexpr int kRows = 64;  // query rows per workgroup (one wave)
 template <int D, int BN>
 __global__ __launch_bounds__(kRows) void fwd_fp32_kernel(
     const float* __restrict__ Q, const float* __restrict__ KV,
-    float* __restrict__ Oacc, float* __restrict__ LSEacc, int BH, int Lq,
+    float* __restrict__ Oacc, float* __restrict__ LSEacc, int BH, int H, int G, int Lq,
     int Lk, int n_qt, int diag, float c2) {
   __shared__ float ks[BN][D];
   __shared__ float vs[BN][D];
@@ -28,9 +28,11 @@ __global__ __launch_bounds__(kRows) void fwd_fp32_kernel(
   const int bh = blockIdx.x / n_qt;
   const int q0 = (blockIdx.x % n_qt) * kRows;
   const int qi = q0 + lane;
+  // Groups of G query heads share one key/value head.
+  const int kvbh = (bh / H) * (H / G) + (bh % H) / G;
   const float* Qp = Q + (size_t)bh * Lq * D;
-  const float* Kp = KV + (size_t)bh * Lk * D;
-  const float* Vp = KV + ((size_t)BH + bh) * Lk * D;
+  const float* Kp = KV + (size_t)kvbh * Lk * D;
+  const float* Vp = KV + ((size_t)(BH / G) + kvbh) * Lk * D;
 
   float qr[D], acc[D];
 #pragma unroll
@@ -113,7 +115,7 @@ hipError_t launch(const float* q, const float* kv, float* o, float* lse,
   const long long grid = (long long)n_qt * BH;
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL((fwd_fp32_kernel<D, BN>), dim3((unsigned)grid), dim3(kRows),
-                     0, a.stream, q, kv, o, lse, BH, a.Lq, a.Lk, n_qt, a.diag,
+                     0, a.stream, q, kv, o, lse, BH, a.H, a.H / a.Hkv, a.Lq, a.Lk, n_qt, a.diag,
                      a.scale * kLog2e);
   return hipGetLastError();
 }

@@ -9,9 +9,9 @@
 
 // Validated, resolved shape of one call.
 struct ra_shape {
-  int B, H, Lq, Lk, D, dtype, elem;
+  int B, H, Hkv, Lq, Lk, D, dtype, elem;  // Hkv divides H
   float scale;
-  int64_t bh, q_rows, kv_rows;
+  int64_t bh, q_rows, kv_rows;  // bh = B*H; kv_rows = B*Hkv*Lk
 };
 
 int ra_fail(int code, const char* fmt, ...);

@@ -339,6 +339,7 @@ struct LdsOffsets {
 // ---- launchers (host side, defined in the .hip sources) --------------------
 struct ra_launch {
   int B, H, Lq, Lk, D;
+  int Hkv;           // key/value heads (divides H)
   float scale;       // resolved (never 0)
   int diag;          // causal diagonal block: mask key j > query i (local)
   int q_chunk, k_chunk;

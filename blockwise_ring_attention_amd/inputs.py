@@ -24,12 +24,14 @@ def _rng(seed: int, cfg_id: int, tensor: str, block: int) -> np.random.Generator
 
 def draw(cfg: ShareConfig, tensor: str, block: int, seed: int = 0,
          length: int | None = None) -> torch.Tensor:
-    """One [B, H, length, d] block of ``tensor`` in the config's dtype (CPU).
+    """One [B, heads, length, d] block of ``tensor`` in the config's dtype
+    (CPU); keys and values have the config's key/value head count.
 
     Values are drawn in float32 and rounded to bf16 with round-to-nearest-even
     for bf16 configs, so both consumers see identical rounded inputs."""
     L = cfg.block_len if length is None else length
-    shape = (cfg.batch, cfg.heads, L, cfg.head_dim)
+    heads = cfg.n_kv_heads if tensor in ("k", "v") else cfg.heads
+    shape = (cfg.batch, heads, L, cfg.head_dim)
     dist = cfg.dist(tensor)
     g = _rng(seed, cfg.cfg_id, tensor, block)
     if dist.kind == "normal":
@@ -51,7 +53,7 @@ def draw(cfg: ShareConfig, tensor: str, block: int, seed: int = 0,
 
 
 def draw_kv(cfg: ShareConfig, block: int, seed: int = 0) -> torch.Tensor:
-    """Packed key/value block [2, B, H, L, d]: index 0 = K, 1 = V."""
+    """Packed key/value block [2, B, Hkv, L, d]: index 0 = K, 1 = V."""
     k = draw(cfg, "k", block, seed)
     v = draw(cfg, "v", block, seed)
     return torch.stack([k, v], dim=0)

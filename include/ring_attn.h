@@ -18,12 +18,18 @@
  *   memory.  All work is enqueued asynchronously on the given hipStream_t
  *   (passed as void*; NULL = the null stream); a device fault surfaces at the
  *   caller's next synchronisation.
- * - Layouts are dense row-major, no strides:
- *     q, dout          [B, H, Lq, d]      (dtype of ra_dims.dtype)
- *     kv_block         [2, B, H, Lk, d]   (index 0 = K, 1 = V; one copy moves it)
- *     o_acc, dq_acc    [B, H, Lq, d]      float32
- *     lse_acc, delta   [B, H, Lq]         float32
- *     dkv_io           [2, B, H, Lk, d]   float32 (0 = dK, 1 = dV)
+ * - Layouts are dense row-major, no strides (H = ra_dims.heads query heads,
+ *   Hkv = ra_dims.kv_heads key/value heads):
+ *     q, dout          [B, H, Lq, d]        (dtype of ra_dims.dtype)
+ *     kv_block         [2, B, Hkv, Lk, d]   (index 0 = K, 1 = V; one copy moves it)
+ *     o_acc, dq_acc    [B, H, Lq, d]        float32
+ *     lse_acc, delta   [B, H, Lq]           float32
+ *     dkv_io           [2, B, Hkv, Lk, d]   float32 (0 = dK, 1 = dV)
+ * - Shared key/value heads (MQA / GQA: several query heads share one
+ *   key/value head; kongchang "Ring Attention" knowledge page, facts list):
+ *   query head h attends to key/value head h / (H / Hkv), i.e. consecutive
+ *   groups of H / Hkv query heads share one.  Hkv == H is ordinary multi-head
+ *   attention, Hkv == 1 is MQA.
  * - Positions are global: member r's query i sits at r*Lq + i and key j of
  *   block kb at kb*Lk + j.  Under the causal mask key j is visible to query
  *   i iff its position is <= the query's (the diagonal is visible).  Causal
@@ -72,12 +78,13 @@ enum { RA_BF16 = 0, RA_FP32 = 1 };
  * the lengths may be 0 (then the call does nothing and returns RA_OK). */
 typedef struct ra_dims {
   int32_t batch;
-  int32_t heads;
+  int32_t heads;     /* H: query heads */
   int32_t q_len;     /* Lq: query rows held by the member */
   int32_t kv_len;    /* Lk: tokens per key/value block */
   int32_t head_dim;  /* d */
   int32_t dtype;     /* RA_BF16 or RA_FP32: dtype of q, kv_block and dout */
   float scale;       /* > 0; 0 => 1/sqrt(head_dim); negative is rejected */
+  int32_t kv_heads;  /* Hkv: key/value heads, dividing heads; 0 => heads */
 } ra_dims;
 
 /* Version of this ABI (major * 100 + minor). */
@@ -112,7 +119,7 @@ int ring_attn_fwd(const void* q, const void* kv_block, int ring_rank,
  *     mu = max(lse_a, lse_b), w_x = exp(lse_x - mu),
  *     lse_a <- mu + ln(w_a + w_b),  o_a <- (w_a o_a + w_b o_b) / (w_a + w_b)
  * with (0, -inf) as the identity on either side.  Shapes: o [B,H,Lq,d],
- * lse [B,H,Lq] (kv_len is ignored).  a and b must not overlap. */
+ * lse [B,H,Lq] (kv_len and kv_heads are ignored).  a and b must not overlap. */
 int ring_attn_combine(float* o_a, float* lse_a, const float* o_b,
                       const float* lse_b, const ra_dims* dims, void* stream);
 
@@ -134,6 +141,8 @@ int ring_attn_bwd_prep(const float* o, const void* dout, float* delta,
  *     dq_acc += dQ  (this block's contribution to the member's dQ)
  *     dkv_io += [dK_kb, dV_kb]  (this member's contribution to block kb)
  * so a travelling dK/dV partial can collect every member's contribution.
+ * With shared key/value heads, dK/dV of a key/value head sums the
+ * contributions of every query head of its group.
  * bf16 only (RA_ERR_UNSUPPORTED for fp32).  A future block under the causal
  * mask is a no-op.  dq_acc and dkv_io must not overlap each other or any
  * input. */
@@ -155,7 +164,7 @@ int ring_attn_bwd(const void* q, const void* kv_block, const void* dout,
  * is never a gather of all blocks.
  *
  * kv_pool: HOST array of ring_size device pointers; kv_pool[kb] is block kb
- *          ([2,B,H,Lk,d]).  Entries that the causal mask never needs (kb >
+ *          ([2,B,Hkv,Lk,d]).  Entries that the causal mask never needs (kb >
  *          ring_rank) may be NULL.  kv_pool[ring_rank] is used in place
  *          (the member's own block needs no hop).
  * slots:   two device buffers of one block each.
@@ -173,7 +182,7 @@ int ring_emu_fwd(const void* q, const void* const* kv_pool, void* slot0,
                  void* main_stream, void* side_stream);
 
 /* Backward share through the emulator.  For each step the block's travelling
- * dK/dV partial dkv_pool[kb] (fp32 [2,B,H,Lk,d], device) is brought into a
+ * dK/dV partial dkv_pool[kb] (fp32 [2,B,Hkv,Lk,d], device) is brought into a
  * receive slot with the key/value block, this member's contribution is added
  * there, and the slot is copied back to dkv_pool[kb] (the hop to the next
  * member), so on return dkv_pool[kb] += this member's dK/dV for every block

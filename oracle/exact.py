@@ -16,6 +16,12 @@ seams.  The oracle therefore writes out the definition directly:
 and materialises S one tile of query rows at a time (a plain memory bound,
 not a reordering of the arithmetic: each row is computed whole).  A row with
 no allowed key gets O_i = 0 and LSE_i = -inf.
+
+Shared key/value heads (MQA / GQA, named on the kongchang "Ring Attention"
+knowledge page, facts list, as sharing key-value heads): with H query heads
+and Hkv key/value heads, query head h uses key/value head h // (H // Hkv), and
+the gradient of a shared key/value head is the sum over the query heads that
+use it.  Hkv == H is ordinary multi-head attention.
 """
 from __future__ import annotations
 
@@ -41,6 +47,19 @@ def _scale(d: int, scale: float | None) -> float:
     return 1.0 / np.sqrt(d) if scale is None else float(scale)
 
 
+def _check_heads(H: int, k) -> int:
+    """The key/value head count, which must divide the query head count."""
+    Hkv = k.shape[1]
+    if Hkv < 1 or H % Hkv != 0:
+        raise ValueError(f"{Hkv} key/value heads do not divide {H} query heads")
+    return Hkv
+
+
+def _kv_head(h: int, H: int, Hkv: int) -> int:
+    """Key/value head of query head h: consecutive groups of H / Hkv."""
+    return h // (H // Hkv)
+
+
 def _scores(qt, k, qpos_t, kpos, causal, scale):
     s = scale * (qt @ k.T)
     if causal:
@@ -52,26 +71,29 @@ def attention(q, k, v, q_pos, k_pos, causal: bool, scale: float | None = None,
               row_tile: int = 256):
     """Exact attention of the rows ``q`` against the keys ``k`` / values ``v``.
 
-    q: [B, H, Lq, d]; k, v: [B, H, Lk, d]; q_pos: [Lq]; k_pos: [Lk] global
-    positions.  Returns (o [B, H, Lq, d], lse [B, H, Lq]) in float64."""
+    q: [B, H, Lq, d]; k, v: [B, Hkv, Lk, d] with Hkv dividing H; q_pos: [Lq];
+    k_pos: [Lk] global positions.  Returns (o [B, H, Lq, d], lse [B, H, Lq])
+    in float64."""
     q, k, v = _as64(q), _as64(k), _as64(v)
     q_pos = np.asarray(q_pos, dtype=np.int64)
     k_pos = np.asarray(k_pos, dtype=np.int64)
     B, H, Lq, d = q.shape
+    Hkv = _check_heads(H, k)
     sc = _scale(d, scale)
     o = np.zeros((B, H, Lq, v.shape[-1]))
     lse = np.full((B, H, Lq), -np.inf)
     for b in range(B):
         for h in range(H):
+            kh = _kv_head(h, H, Hkv)
             for r0 in range(0, Lq, row_tile):
                 r1 = min(Lq, r0 + row_tile)
-                s = _scores(q[b, h, r0:r1], k[b, h], q_pos[r0:r1], k_pos, causal, sc)
+                s = _scores(q[b, h, r0:r1], k[b, kh], q_pos[r0:r1], k_pos, causal, sc)
                 m = s.max(axis=1)
                 live = np.isfinite(m)
                 m_safe = np.where(live, m, 0.0)
                 e = np.exp(s - m_safe[:, None])
                 l = e.sum(axis=1)
-                num = e @ v[b, h]
+                num = e @ v[b, kh]
                 o[b, h, r0:r1] = np.where(live[:, None], num / np.where(live, l, 1.0)[:, None], 0.0)
                 lse[b, h, r0:r1] = np.where(live, m_safe + np.log(np.where(live, l, 1.0)), -np.inf)
     return o, lse
@@ -84,11 +106,14 @@ def attention_grads(q, k, v, do, q_pos, k_pos, causal: bool,
     With P = softmax(S + M) row-wise and delta_i = <dO_i, O_i>:
         dV = P^T dO,  dP = dO V^T,  dS = P * (dP - delta),
         dQ = scale * dS K,  dK = scale * dS^T Q.
-    Returns (dq, dk, dv, o, lse), all float64."""
+    With shared key/value heads, dK and dV of a key/value head sum the
+    contributions of its query heads.  Returns (dq, dk, dv, o, lse), all
+    float64; dk and dv have the key/value head count."""
     q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
     q_pos = np.asarray(q_pos, dtype=np.int64)
     k_pos = np.asarray(k_pos, dtype=np.int64)
     B, H, Lq, d = q.shape
+    Hkv = _check_heads(H, k)
     sc = _scale(d, scale)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
@@ -97,9 +122,10 @@ def attention_grads(q, k, v, do, q_pos, k_pos, causal: bool,
     lse = np.full((B, H, Lq), -np.inf)
     for b in range(B):
         for h in range(H):
+            kh = _kv_head(h, H, Hkv)
             for r0 in range(0, Lq, row_tile):
                 r1 = min(Lq, r0 + row_tile)
-                s = _scores(q[b, h, r0:r1], k[b, h], q_pos[r0:r1], k_pos, causal, sc)
+                s = _scores(q[b, h, r0:r1], k[b, kh], q_pos[r0:r1], k_pos, causal, sc)
                 m = s.max(axis=1)
                 live = np.isfinite(m)
                 m_safe = np.where(live, m, 0.0)
@@ -107,14 +133,14 @@ def attention_grads(q, k, v, do, q_pos, k_pos, causal: bool,
                 l = np.where(live, e.sum(axis=1), 1.0)
                 p = e / l[:, None]
                 p[~live] = 0.0
-                ot = p @ v[b, h]
+                ot = p @ v[b, kh]
                 o[b, h, r0:r1] = ot
                 lse[b, h, r0:r1] = np.where(live, m_safe + np.log(l), -np.inf)
                 dot = do[b, h, r0:r1]
                 delta = (dot * ot).sum(axis=1)
-                dp = dot @ v[b, h].T
+                dp = dot @ v[b, kh].T
                 ds = p * (dp - delta[:, None])
-                dq[b, h, r0:r1] = sc * (ds @ k[b, h])
-                dk[b, h] += sc * (ds.T @ q[b, h, r0:r1])
-                dv[b, h] += p.T @ dot
+                dq[b, h, r0:r1] = sc * (ds @ k[b, kh])
+                dk[b, kh] += sc * (ds.T @ q[b, h, r0:r1])
+                dv[b, kh] += p.T @ dot
     return dq, dk, dv, o, lse

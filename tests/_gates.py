@@ -71,10 +71,12 @@ def oracle_rows(host, heads, rows):
     k_pos = np.concatenate([oracle.positions(b, L) for b in blocks])
     o = np.zeros((cfg.batch, len(heads), len(rows), cfg.head_dim))
     lse = np.zeros((cfg.batch, len(heads), len(rows)))
+    H, Hkv = cfg.heads, host.kv[blocks[0]].shape[2]
     for b in range(cfg.batch):
         for i, h in enumerate(heads):
-            k = torch.cat([host.kv[kb][0, b:b + 1, h:h + 1] for kb in blocks], dim=2)
-            v = torch.cat([host.kv[kb][1, b:b + 1, h:h + 1] for kb in blocks], dim=2)
+            kh = oracle.exact._kv_head(h, H, Hkv)  # the oracle's own head grouping
+            k = torch.cat([host.kv[kb][0, b:b + 1, kh:kh + 1] for kb in blocks], dim=2)
+            v = torch.cat([host.kv[kb][1, b:b + 1, kh:kh + 1] for kb in blocks], dim=2)
             qh = host.q[b:b + 1, h:h + 1, rows]
             ob, lb = oracle.attention(qh, k, v, q_pos, k_pos, cfg.causal)
             o[b, i] = ob[0, 0]

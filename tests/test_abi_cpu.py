@@ -38,12 +38,13 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.ring_attn_version() == 100
+    assert lib.ring_attn_version() == 200
     assert lib.ring_attn_last_error() == b""
 
 
 def _dims(**kw):
-    base = dict(batch=1, heads=2, q_len=64, kv_len=64, head_dim=128, dtype=0, scale=0.0)
+    base = dict(batch=1, heads=2, q_len=64, kv_len=64, head_dim=128, dtype=0, scale=0.0,
+                kv_heads=0)
     base.update(kw)
     return _lib.Dims(*base.values())
 
@@ -82,6 +83,9 @@ def test_unsupported_and_invalid_dims(lib):
     assert _fwd(lib, _dims(q_len=64, kv_len=32)) == -1           # causal needs equal blocks
     assert _fwd(lib, _dims(scale=float("inf"))) == -1
     assert _fwd(lib, _dims(scale=-0.5)) == -1
+    assert _fwd(lib, _dims(heads=4, kv_heads=3)) == -1             # must divide heads
+    assert _fwd(lib, _dims(heads=4, kv_heads=8)) == -1
+    assert _fwd(lib, _dims(heads=4, kv_heads=-2)) == -1
     # the backward is bf16-only
     d = _dims(dtype=1)
     assert lib.ring_attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, 1, 1, 64, 64, FAKE, FAKE,

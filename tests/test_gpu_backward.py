@@ -12,13 +12,22 @@ from tests._gates import check, seam_rows
 pytestmark = pytest.mark.gpu
 
 
-def _oracle_grads(host, heads=None, rows=None):
+def _oracle_grads(host, heads=None, rows=None, kv_head=None):
+    """Oracle dQ and per-block dK/dV: every head (default), the given query
+    heads of a multi-head share, or the query heads of one shared key/value
+    head (kv_head)."""
     cfg = host.cfg
     L = cfg.block_len
     blocks = sorted(host.kv)
-    hs = list(range(cfg.heads)) if heads is None else heads
-    k = torch.cat([host.kv[b][0][:, hs] for b in blocks], dim=2)
-    v = torch.cat([host.kv[b][1][:, hs] for b in blocks], dim=2)
+    if kv_head is not None:
+        G = cfg.heads // host.kv[blocks[0]].shape[2]
+        hs, ks = list(range(kv_head * G, (kv_head + 1) * G)), [kv_head]
+    elif heads is None:
+        hs, ks = list(range(cfg.heads)), list(range(host.kv[blocks[0]].shape[2]))
+    else:
+        hs = ks = heads
+    k = torch.cat([host.kv[b][0][:, ks] for b in blocks], dim=2)
+    v = torch.cat([host.kv[b][1][:, ks] for b in blocks], dim=2)
     q = host.q[:, hs]
     do = host.dout[:, hs]
     q_pos = oracle.positions(host.rank, L)
@@ -138,3 +147,46 @@ def test_causal_independence_bitwise():
     assert torch.equal(a.o_acc[:, :, :p + 1], b.o_acc[:, :, :p + 1])
     assert torch.equal(a.lse_acc[:, :, :p + 1], b.lse_acc[:, :, :p + 1])
     assert torch.equal(a.dq_acc[:, :, :p + 1], b.dq_acc[:, :, :p + 1])
+
+
+@pytest.mark.parametrize("kv_heads", [1, 2])
+def test_shared_kv_heads_backward(kv_heads):
+    """MQA (one key/value head) and GQA (two, for four query heads): dK/dV of
+    a shared head sums its query heads' contributions (one launch per group
+    member), element by element against the oracle."""
+    cfg = ShareConfig(98, f"shared-kv{kv_heads}", "bf16", 1, 4, 128, 3, 200, (2,), True,
+                      256, 64, backward=True, kv_heads=kv_heads)
+    host = share.make_host_share(cfg, 2, seed=8, backward=True)
+    assert host.kv[0].shape[2] == kv_heads
+    dev = _run(host)
+    dq_ref, per_block = _oracle_grads(host)
+    check("dq", dev.dq_acc, dq_ref, "bf16")
+    for b, (dk_ref, dv_ref) in per_block.items():
+        check(f"dk[{b}]", dev.dkv_pool[b][0], dk_ref, "bf16")
+        check(f"dv[{b}]", dev.dkv_pool[b][1], dv_ref, "bf16")
+
+
+def test_shared_kv_heads_full_size():
+    """LWM-7B-shaped training share with eight key/value heads for 32 query
+    heads (rank 3 of 4, 8192 tokens per member): dQ on sampled rows, dK/dV
+    of one shared head against its four query heads' full rows."""
+    cfg = ShareConfig(99, "gqa-train", "bf16", 1, 32, 128, 4, 8192, (3,), True, 256, 64,
+                      backward=True, kv_heads=8)
+    print("gqa: generating inputs", flush=True)
+    host = share.make_host_share(cfg, 3, backward=True)
+    print("gqa: running forward + backward share", flush=True)
+    dev = _run(host)
+    rng = np.random.default_rng(9)
+    rows = seam_rows(cfg.block_len, cfg.q_chunk, rng, 12)
+    heads = sorted(rng.choice(cfg.heads, size=3, replace=False).tolist())
+    print(f"gqa: oracle dq on {len(rows)} rows of heads {heads}", flush=True)
+    for h in heads:
+        dq_ref, _ = _oracle_grads(host, kv_head=h // 4, rows=rows)
+        check(f"dq h{h}", dev.dq_acc[:, [h]][:, :, rows], dq_ref[:, [h % 4]], "bf16")
+    kh = int(rng.integers(8))
+    print(f"gqa: oracle dk/dv of key/value head {kh}", flush=True)
+    _, per_block = _oracle_grads(host, kv_head=kh)
+    for kb, (dk_ref, dv_ref) in per_block.items():
+        check(f"dk[{kb}] kvh{kh}", dev.dkv_pool[kb][0][:, [kh]], dk_ref, "bf16")
+        check(f"dv[{kb}] kvh{kh}", dev.dkv_pool[kb][1][:, [kh]], dv_ref, "bf16")
+    assert torch.isfinite(dev.dq_acc).all()

@@ -190,3 +190,17 @@ def test_full_size_sampled_rows(cfg_id):
     check_lse("lse", dev.lse_acc[:, heads][:, :, rows], lse_ref)
     # every row finite, and every LSE at least the largest single score
     assert torch.isfinite(dev.o_acc).all() and torch.isfinite(dev.lse_acc).all()
+
+
+@pytest.mark.parametrize("kv_heads,dtype", [(1, "bf16"), (2, "bf16"), (2, "fp32")])
+def test_shared_kv_heads_forward(kv_heads, dtype):
+    """MQA / GQA: four query heads over one or two key/value heads, causal
+    ragged share, element by element against the oracle."""
+    cfg = ShareConfig(97, f"shared-kv{kv_heads}", dtype, 1, 4, 128, 3, 200, (2,), True,
+                      256 if dtype == "bf16" else 64, 64, kv_heads=kv_heads)
+    host = share.make_host_share(cfg, 2, seed=4)
+    assert host.kv[0].shape[2] == kv_heads
+    dev, _ = _run(host)
+    o_ref, lse_ref = _full_oracle(host)
+    check("o_acc", dev.o_acc, o_ref, dtype)
+    check_lse("lse", dev.lse_acc, lse_ref)

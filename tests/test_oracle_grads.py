@@ -96,3 +96,24 @@ def test_member_contributions_sum_to_full_gradient():
         dv_sum += dv_r
     np.testing.assert_allclose(dk_sum, dk_f, atol=1e-12)
     np.testing.assert_allclose(dv_sum, dv_f, atol=1e-12)
+
+
+@pytest.mark.parametrize("kv_heads", [1, 2])
+def test_shared_kv_heads_autograd_fp64(kv_heads):
+    """Shared key/value heads: dK / dV of a key/value head sum over its query
+    heads.  Checked against torch fp64 autograd through SDPA's grouped route."""
+    rng = np.random.default_rng(43)
+    B, H, L, d = 1, 4, 40, 16
+    q, do = rng.standard_normal((B, H, L, d)), rng.standard_normal((B, H, L, d))
+    k, v = rng.standard_normal((B, kv_heads, L, d)), rng.standard_normal((B, kv_heads, L, d))
+    pos = np.arange(L)
+    dq, dk, dv, o, _ = attention_grads(q, k, v, do, pos, pos, True, row_tile=16)
+    assert dk.shape == k.shape and dv.shape == v.shape
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True,
+                                                          enable_gqa=True)
+    to.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(o, to.detach().numpy(), atol=1e-12)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12)

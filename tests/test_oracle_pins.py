@@ -157,3 +157,25 @@ def test_closed_forms():
     o2, l2 = attention(q, k[:, :, perm], v[:, :, perm], pos, pos, False)
     np.testing.assert_allclose(o2, o1, atol=1e-13)
     np.testing.assert_allclose(l2, l1, atol=1e-13)
+
+
+@pytest.mark.parametrize("kv_heads", [1, 2])
+def test_shared_kv_heads_library_sdpa_fp64(kv_heads):
+    """Shared key/value heads (MQA / GQA): the oracle against torch SDPA's own
+    grouped-head route (enable_gqa), fp64 CPU, causal over global positions."""
+    rng = np.random.default_rng(6)
+    B, H, L, d = 2, 4, 64, 16
+    q = _rand(rng, B, H, L, d)
+    k, v = _rand(rng, B, kv_heads, 2 * L, d), _rand(rng, B, kv_heads, 2 * L, d)
+    q_pos, k_pos = positions(1, L), np.arange(2 * L)
+    o, lse = attention(q, k, v, q_pos, k_pos, True, row_tile=24)
+    mask = torch.from_numpy(k_pos[None, :] <= q_pos[:, None])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=mask,
+        enable_gqa=True)
+    np.testing.assert_allclose(o, ref.numpy(), atol=1e-12, rtol=0)
+    # query head h reads key/value head h // (H // kv_heads): a contiguous group
+    kk = torch.from_numpy(k).repeat_interleave(H // kv_heads, dim=1)
+    s = torch.from_numpy(q) @ kk.transpose(-1, -2) / math.sqrt(d)
+    s = s.masked_fill(~mask, float("-inf"))
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), atol=1e-12, rtol=0)

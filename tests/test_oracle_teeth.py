@@ -74,3 +74,14 @@ def test_planted_missing_max_shift_term_is_caught(monkeypatch):
             s = np.where(np.asarray(k_pos)[None, None, None, :] > np.asarray(q_pos)[None, None, :, None], -np.inf, s)
         return o, lse - s.max(axis=-1)
     assert not _pin_brute(bad_attention)
+
+
+def test_planted_interleaved_kv_groups_are_caught(monkeypatch):
+    """Query head h must read key/value head h // (H / Hkv) (contiguous groups);
+    the interleaved h % Hkv slip must fail the library grouped-head pin."""
+
+    from tests.test_oracle_pins import test_shared_kv_heads_library_sdpa_fp64 as pin
+    pin(2)  # the unmodified oracle passes
+    monkeypatch.setattr(oa, "_kv_head", lambda h, H, Hkv: h % Hkv)
+    with pytest.raises(AssertionError):
+        pin(2)
