@@ -14,6 +14,12 @@ Throughput is causal-adjusted: 4*d flops per unmasked (query, key) pair for
 the forward and 10*d for the backward (which recomputes the scores), over
 r*L^2 + L(L+1)/2 pairs per head for member r with blocks of L tokens.
 
+``--decode`` times the decode-shaped step instead: 8 sequences, one new
+query row each, 32 heads of 128 (``--kv-heads`` for shared key/value heads),
+against one member's 16384-token share of the key/value cache.  That step
+streams the key/value block from HBM once, so it reports HBM GB/s of its
+algorithmic bytes against the 8 TB/s peak.
+
 Prints one JSON line.  ``--gpus`` above 1 is refused: this benchmark runs one
 member's share on one GPU.
 """
@@ -30,6 +36,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 METRIC = "causal-adjusted attention TFLOP/s per GPU (fwd, fwd+bwd); % of bf16 MFMA peak"
 FWD_FLOPS_PER_PAIR_PER_D = 4
 BWD_FLOPS_PER_PAIR_PER_D = 10
@@ -55,6 +62,9 @@ def _parse():
     ap.add_argument("--kv-heads", type=int, default=0,
                     help="key/value heads shared by groups of the 32 query heads (MQA / GQA); "
                          "0 (default): 32, ordinary multi-head attention")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the decode-shaped step (few query rows against a long "
+                         "key/value block; HBM-bound) instead of the training share")
     ap.add_argument("--trace-overlap", metavar="KERNEL_TRACE_CSV",
                     help="no GPU: read a rocprofv3 --kernel-trace CSV of this benchmark and "
                          "report how much of the ring-hop copy time overlaps the attention "
@@ -64,7 +74,8 @@ def _parse():
 
 # Kernel-name fragments of the attention kernels and of the emulated ring
 # hop (hipMemcpyAsync device-to-device copies run as copy kernels).
-_ATTN_KERNELS = ("fwd_bf16_kernel", "fwd_fp32_kernel", "dq_kernel", "dkv_kernel")
+_ATTN_KERNELS = ("fwd_bf16_kernel", "fwd_fp32_kernel", "dq_kernel", "dkv_kernel",
+                 "decode_kernel", "fold_kernel")
 _COPY_KERNEL = "copyBuffer"
 
 
@@ -105,21 +116,23 @@ def _copy_calibration():
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_lwm7b_fwd_bwd.json")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_lwm7b.json")
 KERNEL_SOURCES = {
     "fwd_bf16": ["blockwise_ring_attention_amd/csrc/fwd_bf16.hip"],
     "bwd_dq": ["blockwise_ring_attention_amd/csrc/bwd_bf16.hip"],
     "bwd_dkv": ["blockwise_ring_attention_amd/csrc/bwd_bf16.hip"],
+    "fwd_decode": ["blockwise_ring_attention_amd/csrc/decode_bf16.hip"],
 }
 COMMON_SOURCE = "blockwise_ring_attention_amd/csrc/ra_common.h"
 
 
-def _profiled(family):
+def _profiled(family, path=TRAFFIC_FILE):
     """The committed counter record of a kernel family (and the file's
     calibration factors), or None when the kernel's source has changed since
     the counters were taken."""
     import hashlib
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
         k = rec["kernels"][family]
         h = hashlib.sha256()
@@ -133,10 +146,10 @@ def _profiled(family):
         return None
 
 
-def _measured_traffic(family):
+def _measured_traffic(family, path=TRAFFIC_FILE):
     """HBM bytes per launch of a kernel family from the committed FETCH_SIZE /
     WRITE_SIZE counter runs (scaled by the copy calibration), or None."""
-    p = _profiled(family)
+    p = _profiled(family, path)
     if p is None:
         return None
     rec, k = p
@@ -161,11 +174,7 @@ def _cpu_baseline(host, cfg, rank, target_s):
 
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = 1
+    cores = _oracle_threads()
     L = cfg.block_len
     blocks = sorted(host.kv)
     k_pos = np.concatenate([oracle.positions(b, L) for b in blocks])
@@ -192,18 +201,172 @@ def _cpu_baseline(host, cfg, rank, target_s):
         heads = int(min(cfg.heads, max(1, round(target_s / max(dt, 1e-3)))))
         dt, pairs = run(list(range(heads)), nrows)
     flops = (FWD_FLOPS_PER_PAIR_PER_D + BWD_FLOPS_PER_PAIR_PER_D) * cfg.head_dim * pairs
-    cpu_model = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            cpu_model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
-    except (OSError, StopIteration):
-        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "cpu_model": cpu_model,
+            "cpu_model": _cpu_model(),
             "sample": (f"fp64 oracle forward + gradients for the last {nrows} query rows of "
                        f"{heads} head(s) against all {len(k_pos)} keys ({pairs} unmasked pairs), "
                        f"{dt:.1f} s"),
             "seconds": round(dt, 2)}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        return "unknown"
+
+
+def _oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def _decode_bytes(cfg, splits):
+    """Algorithmic HBM bytes of one decode step: the split kernel reads q and
+    the key/value block once and writes each split's (o, lse) partial; the
+    fold reads the partials and the accumulator and writes the accumulator."""
+    rows = cfg.batch * cfg.heads * cfg.q_len
+    d = cfg.head_dim
+    kv = 2 * cfg.batch * cfg.n_kv_heads * cfg.kv_len * d * 2
+    part = splits * rows * (d + 1) * 4
+    split_kernel = rows * d * 2 + kv + part
+    fold = part + 2 * rows * (d + 1) * 4
+    return split_kernel, fold
+
+
+def _decode_cpu_baseline(cfg, q, kvs, target_s):
+    """The fp64 oracle, as it stands, on a bounded sample of the decode step:
+    whole (batch, key/value head) groups, in order, until about target_s."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    Lk, G = cfg.kv_len, cfg.heads // cfg.n_kv_heads
+    k_pos = np.concatenate([oracle.positions(i, Lk) for i in range(len(kvs))])
+    q_pos = oracle.positions(len(kvs), Lk, cfg.q_len)
+    done, t0 = 0, time.perf_counter()
+    groups = [(b, kh) for b in range(cfg.batch) for kh in range(cfg.n_kv_heads)]
+    for b, kh in groups:
+        k = torch.cat([kv[0, b:b + 1, kh:kh + 1] for kv in kvs], dim=2)
+        v = torch.cat([kv[1, b:b + 1, kh:kh + 1] for kv in kvs], dim=2)
+        oracle.attention(q[b:b + 1, kh * G:(kh + 1) * G], k, v, q_pos, k_pos, True)
+        done += 1
+        if time.perf_counter() - t0 > target_s:
+            break
+    dt = time.perf_counter() - t0
+    frac = done / len(groups)
+    split_bytes, _ = _decode_bytes(cfg, 1)
+    return {"value": split_bytes * frac / dt / 1e9, "unit": "GB/s", "cores": int(_oracle_threads()),
+            "kind": "oracle", "cpu_model": _cpu_model(),
+            "sample": (f"fp64 oracle attention of {done} of {len(groups)} (batch, key/value head) "
+                       f"groups ({G * cfg.q_len} query rows each against {len(k_pos)} keys), "
+                       f"{dt:.1f} s; bytes are the q and key/value bytes of those groups"),
+            "seconds": round(dt, 2)}
+
+
+def _bench_decode(args):
+    import torch
+
+    from blockwise_ring_attention_amd import _lib
+    from blockwise_ring_attention_amd.configs import DECODE_CONFIGS
+    from blockwise_ring_attention_amd.inputs import draw_decode
+    from dataclasses import replace
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    _lib.load()
+    cfg = replace(DECODE_CONFIGS["decode-lwm7b"], kv_heads=args.kv_heads)
+    mha = cfg.n_kv_heads == cfg.heads
+    t_gen = time.perf_counter()
+    q, kvs = draw_decode(cfg, seed=0)
+    dev = torch.device("cuda:0")
+    qd = q.to(dev)
+    kvd = [kv.to(dev) for kv in kvs]
+    o_acc = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    lse_acc = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    kc = cfg.k_chunk or _lib.ring_attn_decode_chunk(qd, kvd[0])
+    S = _lib.ring_attn_decode_splits(qd, kvd[0], kc)
+    o_part = torch.empty((S,) + tuple(q.shape), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((S,) + tuple(q.shape[:3]), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    main_stream = torch.cuda.current_stream()
+
+    def step():
+        _lib.ring_attn_init_acc(o_acc, lse_acc)
+        for kv in kvd:
+            _lib.ring_attn_fwd_decode(qd, kv, kc, o_acc, lse_acc, o_part, lse_part)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    _lib.ring_attn_timing_enable(True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    w0 = time.perf_counter()
+    ev[0].record(main_stream)
+    for i in range(args.steps):
+        step()
+        ev[i + 1].record(main_stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - w0) * 1e3 / args.steps
+    _lib.ring_attn_timing_enable(False)
+    ms_step = ev[0].elapsed_time(ev[args.steps]) / args.steps
+    step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+
+    split_bytes, fold_bytes = _decode_bytes(cfg, S)
+    nblk = len(kvd)
+    gbs = (split_bytes + fold_bytes) * nblk / (ms_step * 1e-3) / 1e9
+    per_kernel = {}
+    for fam, nbytes in (("fwd_decode", split_bytes), ("decode_fold", fold_bytes)):
+        n, tot = _lib.ring_attn_timing_read(fam)
+        if n == 0:
+            continue
+        avg = tot / n
+        per_kernel[fam] = {"launches": n, "avg_ms": round(avg, 4),
+                           "bytes_per_launch": nbytes,
+                           "gbs": round(nbytes / (avg * 1e-3) / 1e9, 1),
+                           "frac": round(nbytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    dom = "fwd_decode"
+    roofline = {"bound": "hbm", "achieved": per_kernel[dom]["gbs"], "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": per_kernel[dom]["frac"],
+                "traffic": (_measured_traffic(dom, DECODE_TRAFFIC_FILE) if mha else None),
+                "traffic_unit": "HBM bytes per launch", "kernel": dom}
+    result = {
+        "metric": "decode-step HBM GB/s (algorithmic bytes: key/value block read once)",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": (f"decode-lwm7b: batch {cfg.batch}, {cfg.heads} heads"
+                                + (f" ({cfg.n_kv_heads} key/value heads)" if not mha else "")
+                                + f", head_dim {cfg.head_dim}, {cfg.q_len} query row(s) "
+                                f"against {cfg.kv_len} keys"),
+                   "batch": cfg.batch, "heads": cfg.heads, "kv_heads": cfg.n_kv_heads,
+                   "head_dim": cfg.head_dim, "q_len": cfg.q_len, "kv_len": cfg.kv_len,
+                   "blocks": nblk, "k_chunk": kc, "splits": S},
+        "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "decode_rows_per_s": round(cfg.batch * cfg.q_len / (ms_step * 1e-3), 1),
+        "wall_ms_per_step": round(wall, 4),
+        "step_ms_median": round(sorted(step_ms)[len(step_ms) // 2], 4),
+        "step_ms_min": round(min(step_ms), 4),
+        "kernels": per_kernel,
+        "roofline": roofline,
+        "input_setup_s": round(t_gen, 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = _decode_cpu_baseline(cfg, q, kvs, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
 
 
 def main():
@@ -220,6 +383,9 @@ def main():
 
     if args.copy_calibration:
         _copy_calibration()
+        return
+    if args.decode:
+        _bench_decode(args)
         return
 
     import torch

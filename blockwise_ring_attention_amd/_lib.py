@@ -56,6 +56,9 @@ _SIGS = {
     "ring_emu_bwd": ([_vp, ctypes.POINTER(_vp), _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(_vp),
                       _vp, _vp, _i, _i, _i, _i, _i, _vp, ctypes.POINTER(Dims),
                       ctypes.POINTER(ctypes.c_int32), _i, _vp, _vp], _i),
+    "ring_attn_decode_chunk": ([ctypes.POINTER(Dims)], _i),
+    "ring_attn_decode_splits": ([ctypes.POINTER(Dims), _i], _i),
+    "ring_attn_fwd_decode": ([_vp, _vp, _i, _vp, _vp, _vp, _vp, ctypes.POINTER(Dims), _vp], _i),
     "ring_attn_timing_enable": ([_i], _i),
     "ring_attn_timing_read": ([ctypes.c_char_p, ctypes.POINTER(_i), ctypes.POINTER(ctypes.c_double)], _i),
 }
@@ -144,6 +147,48 @@ def ring_attn_fwd(q, kv_block, ring_rank, ring_step, ring_size, causal, q_chunk,
     _check(load().ring_attn_fwd(_ptr(q), _ptr(kv_block), ring_rank, ring_step, ring_size,
                                 int(bool(causal)), q_chunk, k_chunk, _ptr(o_acc), _ptr(lse_acc),
                                 ctypes.byref(dm), _stream(stream)))
+
+
+def _decode_dims(q, kv_block, scale):
+    if kv_block.dim() != 5 or kv_block.shape[0] != 2:
+        raise ValueError("kv_block must be [2, B, Hkv, Lk, d]")
+    return dims(q, kv_block.shape[3], scale, kv_block.shape[2])
+
+
+def ring_attn_decode_chunk(q, kv_block, scale=0.0) -> int:
+    """Keys per split that spread a decode step of these shapes over the chip."""
+    dm = _decode_dims(q, kv_block, scale)
+    rc = load().ring_attn_decode_chunk(ctypes.byref(dm))
+    _check(min(rc, 0))
+    return rc
+
+
+def ring_attn_decode_splits(q, kv_block, k_chunk, scale=0.0) -> int:
+    """Number of key splits S = ceil(Lk / k_chunk) (rows of o_part / lse_part)."""
+    dm = _decode_dims(q, kv_block, scale)
+    rc = load().ring_attn_decode_splits(ctypes.byref(dm), int(k_chunk))
+    _check(min(rc, 0))
+    return rc
+
+
+def ring_attn_fwd_decode(q, kv_block, k_chunk, o_acc, lse_acc, o_part, lse_part, scale=0.0,
+                         stream=None):
+    """Decode-shaped step: folds attention(q, kv_block) (no mask) into
+    (o_acc, lse_acc); o_part [S, B, H, Lq, d] / lse_part [S, B, H, Lq] hold
+    the key splits' partials, S from ring_attn_decode_splits."""
+    _need(kv_block, q.dtype, "kv_block")
+    for t, n in ((o_acc, "o_acc"), (lse_acc, "lse_acc"), (o_part, "o_part"),
+                 (lse_part, "lse_part")):
+        _need(t, torch.float32, n)
+    dm = _decode_dims(q, kv_block, scale)
+    S = ring_attn_decode_splits(q, kv_block, k_chunk, scale)
+    if tuple(o_acc.shape) != tuple(q.shape) or tuple(lse_acc.shape) != tuple(q.shape[:3]):
+        raise ValueError("o_acc / lse_acc do not match q")
+    if o_part.numel() < S * q.numel() or lse_part.numel() < S * lse_acc.numel():
+        raise ValueError(f"o_part / lse_part hold fewer than {S} partials")
+    _check(load().ring_attn_fwd_decode(_ptr(q), _ptr(kv_block), int(k_chunk), _ptr(o_acc),
+                                       _ptr(lse_acc), _ptr(o_part), _ptr(lse_part),
+                                       ctypes.byref(dm), _stream(stream)))
 
 
 def ring_attn_combine(o_a, lse_a, o_b, lse_b, stream=None):

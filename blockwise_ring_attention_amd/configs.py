@@ -94,6 +94,50 @@ CONFIGS: Dict[int, ShareConfig] = {
 }
 
 
+@dataclass(frozen=True)
+class DecodeConfig:
+    """A decode-shaped share: ``q_len`` new query rows per (batch, head) that
+    come after every key, attending to ``blocks`` key/value blocks of
+    ``kv_len`` tokens folded one after another (a member's share of a long
+    key/value cache, or the blocks that reach it around the ring).  The
+    inference use of the method (Ring Attention with Blockwise Transformers,
+    abstract).  ``k_chunk`` = 0 lets the library pick the key split."""
+    cfg_id: int
+    name: str
+    batch: int
+    heads: int
+    head_dim: int
+    q_len: int
+    kv_len: int
+    blocks: int = 1
+    kv_heads: int = 0
+    k_chunk: int = 0
+    dtype: str = "bf16"
+    scale: float = 0.0
+    dists: Dict[str, Dist] = field(default_factory=dict)
+
+    @property
+    def n_kv_heads(self) -> int:
+        return self.kv_heads or self.heads
+
+    @property
+    def block_len(self) -> int:   # default length of a drawn key/value block
+        return self.kv_len
+
+    def dist(self, tensor: str) -> Dist:
+        return self.dists.get(tensor, Dist())
+
+
+DECODE_CONFIGS: Dict[str, DecodeConfig] = {
+    # One decode step of eight sequences for the 7B model's heads (32 x 128)
+    # against one member's 16384-token share of the key/value cache.
+    "decode-lwm7b": DecodeConfig(
+        6, "decode-lwm7b", batch=8, heads=32, head_dim=128, q_len=1, kv_len=16384,
+        dists={"q": Dist("normal", 0.5), "k": Dist("normal", 0.5),
+               "v": Dist("normal", 0.5)}),
+}
+
+
 def scaled(cfg: ShareConfig, **changes) -> ShareConfig:
     """A copy of ``cfg`` with some fields replaced (smaller parity cases)."""
     from dataclasses import replace

@@ -7,6 +7,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -20,8 +21,9 @@ namespace {
 thread_local std::string g_last_error;
 
 // ---- kernel timing: event pairs around launches, kept until read ---------
-enum Kind { kFwdBf16 = 0, kFwdFp32, kBwdDq, kBwdDkv, kKinds };
-const char* const kKindNames[kKinds] = {"fwd_bf16", "fwd_fp32", "bwd_dq", "bwd_dkv"};
+enum Kind { kFwdBf16 = 0, kFwdFp32, kBwdDq, kBwdDkv, kDecode, kDecodeFold, kKinds };
+const char* const kKindNames[kKinds] = {"fwd_bf16", "fwd_fp32",   "bwd_dq",
+                                        "bwd_dkv",  "fwd_decode", "decode_fold"};
 
 struct TimingRec {
   int kind;
@@ -225,9 +227,36 @@ int ra_check_bwd_buffers(const void* q, const void* kv, const void* dout,
   return RA_OK;
 }
 
+namespace {
+
+// Decode-shaped calls: rows of one key/value head group and split limits.
+constexpr int kDecodeMaxRows = 64;
+constexpr int kDecodeMaxSplits = 1 << 16;
+constexpr int kDecodeTileKeys = 128;
+constexpr int kDecodeMaxChunkKeys = 8192;
+
+int ra_check_decode(const ra_shape& s) {
+  if (s.dtype != RA_BF16)
+    return ra_fail(RA_ERR_UNSUPPORTED, "decode step is implemented for bf16 inputs only");
+  if (s.q_rows == 0) return RA_OK;  // (Hkv may be 0 when H is)
+  const int64_t rows = (int64_t)(s.H / s.Hkv) * s.Lq;
+  if (rows > kDecodeMaxRows)
+    return ra_fail(RA_ERR_UNSUPPORTED,
+                   "decode step takes at most %d rows per key/value head group "
+                   "((heads / kv_heads) * q_len = %lld)",
+                   kDecodeMaxRows, (long long)rows);
+  return RA_OK;
+}
+
+int ra_decode_splits(const ra_shape& s, int k_chunk) {
+  return (int)(((int64_t)s.Lk + k_chunk - 1) / k_chunk);
+}
+
+}  // namespace
+
 extern "C" {
 
-int ring_attn_version(void) { return 200; }
+int ring_attn_version(void) { return 201; }
 
 int ring_attn_timing_enable(int on) {
   std::lock_guard<std::mutex> g(g_tmu);
@@ -358,6 +387,72 @@ int ring_attn_bwd(const void* q, const void* kv_block, const void* dout, const f
   const int kb = ra_block_of_step(ring_rank, ring_step, ring_size);
   return ra_bwd_block(q, kv_block, dout, lse, delta, kb, ring_rank, causal, q_chunk,
                       k_chunk, dq_acc, dkv_io, s, (hipStream_t)stream);
+}
+
+int ring_attn_decode_chunk(const ra_dims* dims) {
+  ra_shape s;
+  int rc = ra_check_dims(dims, &s);
+  if (rc) return rc;
+  if ((rc = ra_check_decode(s))) return rc;
+  // Enough splits for about one workgroup per compute unit of the chip (256)
+  // and at most kDecodeMaxChunkKeys keys per split, whole key tiles, and at
+  // least four tiles per split.
+  const int64_t groups = std::max<int64_t>(1, (int64_t)s.B * s.Hkv);
+  const int64_t want = std::max<int64_t>({(int64_t)1, (256 + groups - 1) / groups,
+                                          ((int64_t)s.Lk + kDecodeMaxChunkKeys - 1) /
+                                              kDecodeMaxChunkKeys});
+  int64_t chunk = ((int64_t)s.Lk + want - 1) / want;
+  chunk = (chunk + kDecodeTileKeys - 1) / kDecodeTileKeys * kDecodeTileKeys;
+  chunk = std::max<int64_t>(chunk, 4 * kDecodeTileKeys);
+  return (int)std::min<int64_t>(chunk, std::max<int64_t>(s.Lk, 4 * kDecodeTileKeys));
+}
+
+int ring_attn_decode_splits(const ra_dims* dims, int k_chunk) {
+  ra_shape s;
+  int rc = ra_check_dims(dims, &s);
+  if (rc) return rc;
+  if (k_chunk < 1) return ra_fail(RA_ERR_INVALID, "k_chunk %d must be >= 1", k_chunk);
+  return ra_decode_splits(s, k_chunk);
+}
+
+int ring_attn_fwd_decode(const void* q, const void* kv_block, int k_chunk, float* o_acc,
+                         float* lse_acc, float* o_part, float* lse_part, const ra_dims* dims,
+                         void* stream) {
+  ra_shape s;
+  int rc = ra_check_dims(dims, &s);
+  if (rc) return rc;
+  if ((rc = ra_check_decode(s))) return rc;
+  if (k_chunk < 1) return ra_fail(RA_ERR_INVALID, "k_chunk %d must be >= 1", k_chunk);
+  if ((rc = ra_check_fwd_buffers(q, kv_block, o_acc, lse_acc, s))) return rc;
+  if (s.q_rows == 0 || s.Lk == 0) return RA_OK;  // nothing to attend: identity
+  const int S = ra_decode_splits(s, k_chunk);
+  if (S > kDecodeMaxSplits)
+    return ra_fail(RA_ERR_INVALID, "k_chunk %d gives %d key splits (at most %d)", k_chunk, S,
+                   kDecodeMaxSplits);
+  if ((int64_t)s.B * s.Hkv * S > 0x7fffffffLL || s.q_rows * (s.D / 4) / 256 >= 0x7fffffffLL)
+    return ra_fail(RA_ERR_INVALID, "problem too large for one launch");
+  if (!o_part || !lse_part) return ra_fail(RA_ERR_INVALID, "NULL tensor pointer");
+  const size_t qb = (size_t)s.q_rows * s.D * s.elem;
+  const size_t kvb = (size_t)2 * s.kv_rows * s.D * s.elem;
+  const size_t ob = (size_t)s.q_rows * s.D * 4, lb = (size_t)s.q_rows * 4;
+  const size_t opb = ob * S, lpb = lb * S;
+  const void* other[4] = {q, kv_block, o_acc, lse_acc};
+  const size_t othersz[4] = {qb, kvb, ob, lb};
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(o_part, opb, other[i], othersz[i]) ||
+        overlaps(lse_part, lpb, other[i], othersz[i]))
+      return ra_fail(RA_ERR_INVALID, "o_part / lse_part overlap another buffer");
+  if (overlaps(o_part, opb, lse_part, lpb))
+    return ra_fail(RA_ERR_INVALID, "o_part overlaps lse_part");
+  ra_launch L{s.B, s.H, s.Lq, s.Lk, s.D, s.Hkv, s.scale, 0, 0, k_chunk, (hipStream_t)stream};
+  Timed t(kDecode, L.stream);
+  hipError_t e = ra_launch_decode_split(q, kv_block, o_part, lse_part, k_chunk, S, L);
+  t.done();
+  if (e != hipSuccess) return ra_hip_fail(e, "decode kernel launch");
+  Timed tf(kDecodeFold, L.stream);
+  e = ra_launch_decode_fold(o_acc, lse_acc, o_part, lse_part, s.q_rows, s.D, S, L.stream);
+  tf.done();
+  return e == hipSuccess ? RA_OK : ra_hip_fail(e, "decode fold kernel launch");
 }
 
 }  // extern "C"

@@ -111,37 +111,63 @@ __device__ __forceinline__ int swz(int r) {
 // that the compiler does not order every later LDS read after it; the kernel
 // waits for these loads itself (s_waitcnt vmcnt + barrier) before reading the
 // stage they fill.  The instruction has no register outputs.
+// NT sets the non-temporal cache policy: for data read exactly once (a
+// decode step's key/value stream), which then streams past the L2 instead of
+// displacing it; kernels that re-read tiles from L2 leave it off.
+#define RA_DMA16(SFX) "s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" SFX
+template <bool NT = false>
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds_base) : "memory", "m0");
+  if constexpr (NT)
+    asm volatile(RA_DMA16(" nt") :: "v"(src), "s"(lds_base) : "memory", "m0");
+  else
+    asm volatile(RA_DMA16("") :: "v"(src), "s"(lds_base) : "memory", "m0");
 }
+#undef RA_DMA16
 
 // N consecutive 1 KiB direct-to-LDS copies from a wave-uniform base: copy i
 // reads 16 bytes per lane at sbase + voff[i] + 1024 i and writes them to LDS
 // byte address lds_base + 1024 i + 16*lane.  The instruction offset applies to
 // both the global and the LDS address, so M0 is written once for the group.
-template <int N>
+#define RA_DMA16_G1(SFX) "s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" SFX
+#define RA_DMA16_G2(SFX)                         \
+  "s_mov_b32 m0, %3\n\t"                         \
+  "global_load_lds_dwordx4 %0, %2" SFX "\n\t"    \
+  "global_load_lds_dwordx4 %1, %2 offset:1024" SFX
+#define RA_DMA16_G4(SFX)                                \
+  "s_mov_b32 m0, %5\n\t"                                \
+  "global_load_lds_dwordx4 %0, %4" SFX "\n\t"           \
+  "global_load_lds_dwordx4 %1, %4 offset:1024" SFX "\n\t" \
+  "global_load_lds_dwordx4 %2, %4 offset:2048" SFX "\n\t" \
+  "global_load_lds_dwordx4 %3, %4 offset:3072" SFX
+template <int N, bool NT = false>
 __device__ __forceinline__ void dma16_group(const void* sbase, const uint32_t (&voff)[N],
                                             uint32_t lds_base) {
   static_assert(N == 1 || N == 2 || N == 4, "group size");
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
-  if constexpr (N == 1)
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :: "v"(voff[0]), "s"(sbase), "s"(m0) : "memory", "m0");
-  else if constexpr (N == 2)
-    asm volatile("s_mov_b32 m0, %3\n\t"
-                 "global_load_lds_dwordx4 %0, %2\n\t"
-                 "global_load_lds_dwordx4 %1, %2 offset:1024"
-                 :: "v"(voff[0]), "v"(voff[1]), "s"(sbase), "s"(m0) : "memory", "m0");
-  else
-    asm volatile("s_mov_b32 m0, %5\n\t"
-                 "global_load_lds_dwordx4 %0, %4\n\t"
-                 "global_load_lds_dwordx4 %1, %4 offset:1024\n\t"
-                 "global_load_lds_dwordx4 %2, %4 offset:2048\n\t"
-                 "global_load_lds_dwordx4 %3, %4 offset:3072"
-                 :: "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(sbase), "s"(m0)
-                 : "memory", "m0");
+  if constexpr (N == 1) {
+    if constexpr (NT)
+      asm volatile(RA_DMA16_G1(" nt") :: "v"(voff[0]), "s"(sbase), "s"(m0) : "memory", "m0");
+    else
+      asm volatile(RA_DMA16_G1("") :: "v"(voff[0]), "s"(sbase), "s"(m0) : "memory", "m0");
+  } else if constexpr (N == 2) {
+    if constexpr (NT)
+      asm volatile(RA_DMA16_G2(" nt") :: "v"(voff[0]), "v"(voff[1]), "s"(sbase), "s"(m0)
+                   : "memory", "m0");
+    else
+      asm volatile(RA_DMA16_G2("") :: "v"(voff[0]), "v"(voff[1]), "s"(sbase), "s"(m0)
+                   : "memory", "m0");
+  } else {
+    if constexpr (NT)
+      asm volatile(RA_DMA16_G4(" nt") :: "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]),
+                   "s"(sbase), "s"(m0) : "memory", "m0");
+    else
+      asm volatile(RA_DMA16_G4("") :: "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]),
+                   "s"(sbase), "s"(m0) : "memory", "m0");
+  }
 }
+#undef RA_DMA16_G1
+#undef RA_DMA16_G2
+#undef RA_DMA16_G4
 
 // Direct-to-LDS copy of 4 bytes per lane: lane l's word lands at LDS byte
 // address lds_base + 4*l.  Same contract as dma16.
@@ -187,7 +213,7 @@ __device__ __forceinline__ uint32_t dma_xor(int j) {
 // past L-1 clamped to L-1).
 // The same loads, each under its own full / ragged test with its own M0.
 // Same effect; which form schedules better depends on the kernel.
-template <int D, int BT, int N>
+template <int D, int BT, int N, bool NT = false>
 __device__ __forceinline__ void dma_tile_loads_split(uint32_t tile_lds, const bf16* A, int t0,
                                                      int L, int j0, uint32_t lane_part) {
   constexpr int ROWB = D * 2;
@@ -198,15 +224,15 @@ __device__ __forceinline__ void dma_tile_loads_split(uint32_t tile_lds, const bf
     const uint32_t off = lane_part ^ dma_xor<D>(j);
     if (t0 + BT <= L) {
       const uint32_t voff[1] = {off + (uint32_t)j * 1024};
-      dma16_group<1>(uniform(A + (size_t)t0 * D), voff, lds);
+      dma16_group<1, NT>(uniform(A + (size_t)t0 * D), voff, lds);
     } else {
       const int row = j * (1024 / ROWB) + (int)(off / ROWB);
-      dma16((const char*)(A + (size_t)min(t0 + row, L - 1) * D) + off % ROWB, lds);
+      dma16<NT>((const char*)(A + (size_t)min(t0 + row, L - 1) * D) + off % ROWB, lds);
     }
   }
 }
 
-template <int D, int BT, int N>
+template <int D, int BT, int N, bool NT = false>
 __device__ __forceinline__ void dma_tile_loads(uint32_t tile_lds, const bf16* A, int t0, int L,
                                                int j0, uint32_t lane_part) {
   constexpr int ROWB = D * 2;
@@ -215,14 +241,15 @@ __device__ __forceinline__ void dma_tile_loads(uint32_t tile_lds, const bf16* A,
     uint32_t voff[N];  // (x ^ y) + z: one v_xad_u32 each
 #pragma unroll
     for (int i = 0; i < N; ++i) voff[i] = (lane_part ^ dma_xor<D>(j0 + i)) + (uint32_t)j0 * 1024;
-    dma16_group<N>(uniform(A + (size_t)t0 * D), voff, lds0);
+    dma16_group<N, NT>(uniform(A + (size_t)t0 * D), voff, lds0);
   } else {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int j = j0 + i;
       const uint32_t off = lane_part ^ dma_xor<D>(j);
       const int row = j * (1024 / ROWB) + (int)(off / ROWB);
-      dma16((const char*)(A + (size_t)min(t0 + row, L - 1) * D) + off % ROWB, lds0 + i * 1024);
+      dma16<NT>((const char*)(A + (size_t)min(t0 + row, L - 1) * D) + off % ROWB,
+                lds0 + i * 1024);
     }
   }
 }
@@ -235,8 +262,9 @@ __device__ __forceinline__ void dma_tile_loads(uint32_t tile_lds, const bf16* A,
 // HOLD keeps the lane offset in a register across calls; otherwise it is
 // recomputed at each call (for kernels short of registers).  SPLIT issues
 // each load under its own full / ragged test (dma_tile_loads_split), which
-// measured faster in the forward kernel; otherwise one test per call.
-template <int D, int BT, int NW, bool HOLD = true, bool SPLIT = false>
+// measured faster in the forward kernel; otherwise one test per call.  NT
+// issues the copies with the non-temporal cache policy (see dma16).
+template <int D, int BT, int NW, bool HOLD = true, bool SPLIT = false, bool NT = false>
 struct TileLoader {
   static constexpr int ROWB = D * 2;
   static constexpr int TILEB = BT * ROWB;
@@ -258,9 +286,9 @@ struct TileLoader {
       lp = dma_lane_part<D>(ln);
     }
     if constexpr (SPLIT)
-      dma_tile_loads_split<D, BT, LPW>(tile_lds, A, t0, L, wave * LPW, lp);
+      dma_tile_loads_split<D, BT, LPW, NT>(tile_lds, A, t0, L, wave * LPW, lp);
     else
-      dma_tile_loads<D, BT, LPW>(tile_lds, A, t0, L, wave * LPW, lp);
+      dma_tile_loads<D, BT, LPW, NT>(tile_lds, A, t0, L, wave * LPW, lp);
   }
 };
 
@@ -297,8 +325,8 @@ struct MfmaReadPipeline {
 // issue order, so vmcnt(N) means all but the N most recent are done.
 template <int N>
 __device__ __forceinline__ void wait_vmem_n() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maxima).  The builtin,
@@ -348,6 +376,15 @@ struct ra_launch {
 
 hipError_t ra_launch_fwd_bf16(const void* q, const void* kv, float* o_acc,
                               float* lse_acc, const ra_launch& a);
+// Decode-shaped forward.  ra_launch_decode_split attends the (H / Hkv) * Lq
+// <= 64 rows of each key/value head group to `splits` key splits of k_chunk
+// keys, writing o_part [splits, B, H, Lq, d] / lse_part [splits, B, H, Lq];
+// ra_launch_decode_fold folds them, in split order, into (o_acc, lse_acc).
+hipError_t ra_launch_decode_split(const void* q, const void* kv, float* o_part, float* lse_part,
+                                  int k_chunk, int splits, const ra_launch& a);
+hipError_t ra_launch_decode_fold(float* o_acc, float* lse_acc, const float* o_part,
+                                 const float* lse_part, int64_t rows, int D, int splits,
+                                 hipStream_t stream);
 hipError_t ra_launch_fwd_fp32(const float* q, const float* kv, float* o_acc,
                               float* lse_acc, const ra_launch& a);
 hipError_t ra_launch_init_acc(float* o_acc, float* lse_acc, int64_t rows,

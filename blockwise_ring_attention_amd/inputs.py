@@ -12,7 +12,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from .configs import ShareConfig
+from .configs import DecodeConfig, ShareConfig
 
 TENSOR_ID = {"q": 0, "k": 1, "v": 2, "do": 3}
 
@@ -22,7 +22,7 @@ def _rng(seed: int, cfg_id: int, tensor: str, block: int) -> np.random.Generator
     return np.random.default_rng(ss)
 
 
-def draw(cfg: ShareConfig, tensor: str, block: int, seed: int = 0,
+def draw(cfg: ShareConfig | DecodeConfig, tensor: str, block: int, seed: int = 0,
          length: int | None = None) -> torch.Tensor:
     """One [B, heads, length, d] block of ``tensor`` in the config's dtype
     (CPU); keys and values have the config's key/value head count.
@@ -52,12 +52,20 @@ def draw(cfg: ShareConfig, tensor: str, block: int, seed: int = 0,
     return t
 
 
-def draw_kv(cfg: ShareConfig, block: int, seed: int = 0) -> torch.Tensor:
+def draw_kv(cfg: ShareConfig | DecodeConfig, block: int, seed: int = 0) -> torch.Tensor:
     """Packed key/value block [2, B, Hkv, L, d]: index 0 = K, 1 = V."""
     k = draw(cfg, "k", block, seed)
     v = draw(cfg, "v", block, seed)
     return torch.stack([k, v], dim=0)
 
 
-def torch_dtype(cfg: ShareConfig) -> torch.dtype:
+def draw_decode(cfg: DecodeConfig, seed: int = 0):
+    """Inputs of a decode-shaped share: query rows [B, H, Lq, d] (drawn as
+    block ``cfg.blocks``, the one after every key) and the ``cfg.blocks``
+    packed key/value blocks [2, B, Hkv, Lk, d], in arrival order."""
+    q = draw(cfg, "q", cfg.blocks, seed, length=cfg.q_len)
+    return q, [draw_kv(cfg, i, seed) for i in range(cfg.blocks)]
+
+
+def torch_dtype(cfg: ShareConfig | DecodeConfig) -> torch.dtype:
     return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32

@@ -152,6 +152,39 @@ int ring_attn_bwd(const void* q, const void* kv_block, const void* dout,
                   int k_chunk, float* dq_acc, float* dkv_io,
                   const ra_dims* dims, void* stream);
 
+/* ---- decode-shaped step ---------------------------------------------------
+ * The inference use of the method (Ring Attention with Blockwise
+ * Transformers, abstract: training and inference of long sequences): a few
+ * new query rows -- one decode step, or a short run of Lq draft tokens --
+ * that come after every key of kv_block attend to the whole block, which
+ * may be one member's share of a long key/value cache.  There is no mask
+ * inside the block: every key precedes every query row.  As in
+ * ring_attn_fwd,
+ *     (o_acc, lse_acc) <- (o_acc, lse_acc) (+) attention(q, kv_block)
+ * so blocks arriving around the ring fold in the same way.
+ *
+ * With so few rows the step streams the key/value block from HBM once; to
+ * spread that over the chip the block's keys are split into
+ * S = ceil(Lk / k_chunk) splits of k_chunk keys, attended in parallel, each
+ * giving a normalised partial; the S partials are then folded into the
+ * accumulator in split order.  The caller provides the partials' storage:
+ *     o_part   [S, B, H, Lq, d]  float32
+ *     lse_part [S, B, H, Lq]     float32
+ * which must not overlap each other or any other argument; their contents
+ * on return are unspecified.  Requirements: bf16 inputs
+ * (RA_ERR_UNSUPPORTED otherwise); (H / Hkv) * Lq <= 64, the query rows that
+ * share one key/value head (RA_ERR_UNSUPPORTED otherwise); k_chunk >= 1 and
+ * S <= 65536 (RA_ERR_INVALID).  Lk == 0 leaves the accumulators unchanged.
+ * ring_attn_decode_chunk(dims) returns a k_chunk (> 0) that spreads the
+ * splits over the chip for these dims, or a negative error code;
+ * ring_attn_decode_splits(dims, k_chunk) returns S (>= 0), or a negative
+ * error code. */
+int ring_attn_decode_chunk(const ra_dims* dims);
+int ring_attn_decode_splits(const ra_dims* dims, int k_chunk);
+int ring_attn_fwd_decode(const void* q, const void* kv_block, int k_chunk,
+                         float* o_acc, float* lse_acc, float* o_part,
+                         float* lse_part, const ra_dims* dims, void* stream);
+
 /* ---- single-GPU ring emulator ------------------------------------------
  * Plays one member of a ring of ring_size members on one GPU.  The other
  * members' key/value blocks live in a device pool; the "hop" that would
@@ -200,7 +233,8 @@ int ring_emu_bwd(const void* q, const void* const* kv_pool, void* slot0,
 /* ---- kernel timing (diagnostics) ---------------------------------------
  * While enabled, each attention kernel the library launches is bracketed by
  * a pair of HIP events recorded on the stream the kernel runs on.  Kernel
- * families: "fwd_bf16", "fwd_fp32", "bwd_dq", "bwd_dkv".
+ * families: "fwd_bf16", "fwd_fp32", "bwd_dq", "bwd_dkv", "fwd_decode" (the
+ * split kernel of ring_attn_fwd_decode) and "decode_fold" (its fold).
  * ring_attn_timing_enable(on): on != 0 discards earlier records and starts
  * collecting; 0 stops collecting (records are kept).
  * ring_attn_timing_read(name, &launches, &total_ms): waits for the recorded

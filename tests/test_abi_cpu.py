@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
     names = _declared()
     for n in ("ring_attn_fwd", "ring_attn_combine", "ring_attn_bwd", "ring_attn_bwd_prep",
               "ring_attn_finalize", "ring_attn_init_acc", "ring_attn_last_error",
-              "ring_attn_version", "ring_emu_fwd", "ring_emu_bwd"):
+              "ring_attn_version", "ring_emu_fwd", "ring_emu_bwd", "ring_attn_fwd_decode",
+              "ring_attn_decode_chunk", "ring_attn_decode_splits"):
         assert n in names
     assert sorted(_lib.EXPORTS) == names, "binding and header disagree"
 
@@ -38,7 +39,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.ring_attn_version() == 200
+    assert lib.ring_attn_version() == 201
     assert lib.ring_attn_last_error() == b""
 
 
@@ -99,6 +100,77 @@ def test_empty_problems_are_no_ops(lib):
     assert _fwd(lib, _dims(batch=0), q=None, kv=None, o=None, lse=None) == 0
     d = _dims(heads=0)
     assert lib.ring_attn_combine(None, None, None, None, ctypes.byref(d), None) == 0
+
+
+def _decode(lib, dims, kc=64, q=FAKE, kv=FAKE2, o=ctypes.c_void_p(0x10000000),
+            lse=ctypes.c_void_p(0x20000000), op=ctypes.c_void_p(0x30000000),
+            lp=ctypes.c_void_p(0x40000000)):
+    return lib.ring_attn_fwd_decode(q, kv, kc, o, lse, op, lp,
+                                    ctypes.byref(dims) if dims is not None else None, None)
+
+
+def test_decode_rejects_invalid_and_unsupported(lib):
+    d1 = _dims(q_len=1, kv_len=4096)
+    assert _decode(lib, None) == -1
+    assert _decode(lib, _dims(q_len=1, dtype=1)) == -2                 # bf16 only
+    assert _decode(lib, _dims(heads=8, kv_heads=1, q_len=9)) == -2      # 72 rows per group
+    assert _decode(lib, _dims(heads=2, q_len=65)) == -2
+    assert _decode(lib, d1, kc=0) == -1
+    assert _decode(lib, d1, kc=-5) == -1
+    assert _decode(lib, d1, op=None) == -1
+    assert _decode(lib, d1, lp=None) == -1
+    assert _decode(lib, d1, q=None) == -1
+    assert _decode(lib, _dims(q_len=1, kv_len=70000), kc=1) == -1      # 70000 splits
+    # o_part [S, 1, 2, 1, 128] fp32 with S = 64 spans 64 KiB from 0x30000000
+    assert _decode(lib, d1, lp=ctypes.c_void_p(0x30000000 + 60000)) == -1  # parts overlap
+    assert _decode(lib, d1, op=ctypes.c_void_p(0x10000000 - 1024)) == -1  # overlaps o_acc
+    assert _decode(lib, d1, lp=ctypes.c_void_p(0x1000 + 64)) == -1       # overlaps q
+    assert b"rows per key/value head group" in _decode_msg(lib, _dims(heads=4, kv_heads=1,
+                                                                      q_len=17))
+
+
+def _decode_msg(lib, dims):
+    assert _decode(lib, dims) != 0
+    return lib.ring_attn_last_error()
+
+
+def test_decode_empty_calls_are_no_ops(lib):
+    nul = dict(q=None, kv=None, o=None, lse=None, op=None, lp=None)
+    assert _decode(lib, _dims(q_len=0), **nul) == 0
+    assert _decode(lib, _dims(batch=0, q_len=1), **nul) == 0
+    assert _decode(lib, _dims(heads=0, q_len=1), **nul) == 0
+    # no keys: accumulators unchanged, nothing enqueued
+    assert _decode(lib, _dims(q_len=1, kv_len=0), kv=None, op=None, lp=None) == 0
+
+
+def test_decode_split_planning(lib):
+    def chunk(**kw):
+        return lib.ring_attn_decode_chunk(ctypes.byref(_dims(**kw)))
+
+    def splits(kc, **kw):
+        return lib.ring_attn_decode_splits(ctypes.byref(_dims(**kw)), kc)
+
+    # about one workgroup per compute unit (B * Hkv * S ~ 256), at most 8192
+    # keys per split, whole tiles of 128 keys, at least four tiles
+    assert chunk(batch=1, heads=32, q_len=1, kv_len=16384) == 2048
+    assert chunk(batch=1, heads=32, kv_heads=8, q_len=4, kv_len=16384) == 512
+    assert chunk(batch=8, heads=32, q_len=1, kv_len=16384) == 8192
+    assert chunk(batch=8, heads=32, kv_heads=8, q_len=1, kv_len=16384) == 4096
+    assert chunk(batch=8, heads=32, q_len=1, kv_len=131072) == 8192
+    assert chunk(batch=1, heads=32, q_len=1, kv_len=100) == 512        # at least four tiles
+    assert chunk(batch=1, heads=1, q_len=1, kv_len=1000) == 512
+    assert chunk(q_len=1, dtype=1) == -2
+    assert chunk(heads=8, kv_heads=1, q_len=9) == -2
+    assert splits(2048, heads=32, q_len=1, kv_len=16384) == 8
+    assert splits(200, q_len=1, kv_len=1000) == 5
+    assert splits(1000, q_len=1, kv_len=1000) == 1
+    assert splits(64, q_len=1, kv_len=0) == 0
+    assert splits(0, q_len=1, kv_len=10) == -1
+    for kw in ({"batch": 2, "heads": 16, "kv_heads": 2, "q_len": 4, "kv_len": 777},
+               {"batch": 3, "heads": 5, "q_len": 1, "kv_len": 99999}):
+        kc = chunk(**kw)
+        assert kc > 0 and kc % 128 == 0
+        assert splits(kc, **kw) <= 65536
 
 
 def test_emulator_rejects_bad_schedules(lib):

@@ -179,3 +179,25 @@ def test_shared_kv_heads_library_sdpa_fp64(kv_heads):
     s = torch.from_numpy(q) @ kk.transpose(-1, -2) / math.sqrt(d)
     s = s.masked_fill(~mask, float("-inf"))
     np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), atol=1e-12, rtol=0)
+
+
+def test_decode_rows_after_every_key_library_sdpa_fp64():
+    """Decode-shaped rows (a few new queries placed after every key) under the
+    causal mask reduce to unmasked attention: torch SDPA without a mask, fp64
+    CPU, with grouped key/value heads and three blocks of keys."""
+    rng = np.random.default_rng(8)
+    B, H, Hkv, Lq, Lk, d = 2, 8, 2, 3, 50, 16
+    q = _rand(rng, B, H, Lq, d)
+    k, v = _rand(rng, B, Hkv, 3 * Lk, d), _rand(rng, B, Hkv, 3 * Lk, d)
+    k_pos = np.arange(3 * Lk)
+    q_pos = positions(3, Lk, Lq)          # after blocks 0, 1 and 2
+    o, lse = attention(q, k, v, q_pos, k_pos, True)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), enable_gqa=True)
+    np.testing.assert_allclose(o, ref.numpy(), atol=1e-12, rtol=0)
+    kk = torch.from_numpy(k).repeat_interleave(H // Hkv, dim=1)
+    s = torch.from_numpy(q) @ kk.transpose(-1, -2) / math.sqrt(d)
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), atol=1e-12, rtol=0)
+    o_nc, lse_nc = attention(q, k, v, q_pos, k_pos, False)
+    np.testing.assert_array_equal(o, o_nc)
+    np.testing.assert_array_equal(lse, lse_nc)
