@@ -20,6 +20,10 @@ against one member's 16384-token share of the key/value cache.  That step
 streams the key/value block from HBM once, so it reports HBM GB/s of its
 algorithmic bytes against the 8 TB/s peak.
 
+``--ffn`` times the blockwise feedforward of one member's 16384-token block
+of the 7B model instead (width 4096, hidden 16384, 4096 rows per chunk):
+4·rows·d_model·d_ff flops in two bf16 MFMA products per chunk.
+
 Prints one JSON line.  ``--gpus`` above 1 is refused: this benchmark runs one
 member's share on one GPU.
 """
@@ -65,6 +69,8 @@ def _parse():
     ap.add_argument("--decode", action="store_true",
                     help="time the decode-shaped step (few query rows against a long "
                          "key/value block; HBM-bound) instead of the training share")
+    ap.add_argument("--ffn", action="store_true",
+                    help="time the blockwise feedforward of the member's block instead")
     ap.add_argument("--trace-overlap", metavar="KERNEL_TRACE_CSV",
                     help="no GPU: read a rocprofv3 --kernel-trace CSV of this benchmark and "
                          "report how much of the ring-hop copy time overlaps the attention "
@@ -75,7 +81,7 @@ def _parse():
 # Kernel-name fragments of the attention kernels and of the emulated ring
 # hop (hipMemcpyAsync device-to-device copies run as copy kernels).
 _ATTN_KERNELS = ("fwd_bf16_kernel", "fwd_fp32_kernel", "dq_kernel", "dkv_kernel",
-                 "decode_kernel", "fold_kernel")
+                 "decode_kernel", "fold_kernel", "gemm_tn_kernel")
 _COPY_KERNEL = "copyBuffer"
 
 
@@ -122,6 +128,8 @@ KERNEL_SOURCES = {
     "bwd_dq": ["blockwise_ring_attention_amd/csrc/bwd_bf16.hip"],
     "bwd_dkv": ["blockwise_ring_attention_amd/csrc/bwd_bf16.hip"],
     "fwd_decode": ["blockwise_ring_attention_amd/csrc/decode_bf16.hip"],
+    "ffn_up": ["blockwise_ring_attention_amd/csrc/ffn_bf16.hip"],
+    "ffn_down": ["blockwise_ring_attention_amd/csrc/ffn_bf16.hip"],
 }
 COMMON_SOURCE = "blockwise_ring_attention_amd/csrc/ra_common.h"
 
@@ -369,6 +377,116 @@ def _bench_decode(args):
     print(json.dumps(result), flush=True)
 
 
+FFN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ffn_lwm7b.json")
+
+
+def _ffn_cpu_baseline(x, w1, w2, target_s):
+    """The fp64 oracle, as it stands, on a bounded sample of the rows."""
+    import oracle
+
+    n, t0 = 8, time.perf_counter()
+    while True:
+        oracle.feedforward(x[:n], w1, w2)
+        dt = time.perf_counter() - t0
+        if dt > target_s / 4 or n >= x.shape[0]:
+            break
+        n, t0 = min(x.shape[0], n * 4), time.perf_counter()
+    flops = 4.0 * n * w1.shape[1] * w1.shape[0]
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(_oracle_threads()),
+            "kind": "oracle", "cpu_model": _cpu_model(),
+            "sample": (f"fp64 oracle feedforward of the first {n} of {x.shape[0]} rows "
+                       f"(d_model {w1.shape[1]}, d_ff {w1.shape[0]}), {dt:.1f} s"),
+            "seconds": round(dt, 2)}
+
+
+def _bench_ffn(args):
+    import torch
+
+    from blockwise_ring_attention_amd import _lib
+    from blockwise_ring_attention_amd.configs import FFN_CONFIGS
+    from blockwise_ring_attention_amd.inputs import draw_ffn
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    _lib.load()
+    cfg = FFN_CONFIGS["ffn-lwm7b"]
+    t_gen = time.perf_counter()
+    x, w1, w2 = draw_ffn(cfg, seed=0)
+    dev = torch.device("cuda:0")
+    xd, w1d, w2d = x.to(dev), w1.to(dev), w2.to(dev)
+    hidden = torch.empty((min(cfg.rows, cfg.chunk_rows), cfg.d_ff), dtype=torch.bfloat16,
+                         device=dev)
+    out = torch.empty((cfg.rows, cfg.d_model), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    main_stream = torch.cuda.current_stream()
+
+    def step():
+        _lib.ring_ffn_fwd(xd, w1d, w2d, hidden, out, cfg.chunk_rows)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    _lib.ring_attn_timing_enable(True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    w0 = time.perf_counter()
+    ev[0].record(main_stream)
+    for i in range(args.steps):
+        step()
+        ev[i + 1].record(main_stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - w0) * 1e3 / args.steps
+    _lib.ring_attn_timing_enable(False)
+    ms_step = ev[0].elapsed_time(ev[args.steps]) / args.steps
+    step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    chunks = (cfg.rows + cfg.chunk_rows - 1) // cfg.chunk_rows
+    flops = 4.0 * cfg.rows * cfg.d_model * cfg.d_ff
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    per_kernel = {}
+    for fam in ("ffn_up", "ffn_down"):
+        n, tot = _lib.ring_attn_timing_read(fam)
+        if n == 0:
+            continue
+        avg = tot / n
+        fl = flops / 2 / chunks            # each product is half the flops, per chunk
+        per_kernel[fam] = {"launches": n, "avg_ms": round(avg, 4),
+                           "flops_per_launch": fl,
+                           "tflops": round(fl / (avg * 1e-3) / 1e12, 1),
+                           "frac": round(fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    dom = max(per_kernel, key=lambda f: per_kernel[f]["avg_ms"] * per_kernel[f]["launches"])
+    roofline = {"bound": "mfma", "achieved": per_kernel[dom]["tflops"], "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": per_kernel[dom]["frac"],
+                "traffic": _measured_traffic(dom, FFN_TRAFFIC_FILE),
+                "traffic_unit": "HBM bytes per launch", "kernel": dom}
+    result = {
+        "metric": "blockwise feedforward TFLOP/s (4·rows·d_model·d_ff per pass); % of bf16 MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": (f"ffn-lwm7b: {cfg.rows} rows, d_model {cfg.d_model}, d_ff {cfg.d_ff}, "
+                                f"GELU, {cfg.chunk_rows} rows per chunk"),
+                   "rows": cfg.rows, "d_model": cfg.d_model, "d_ff": cfg.d_ff,
+                   "chunk_rows": cfg.chunk_rows},
+        "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "wall_ms_per_step": round(wall, 4),
+        "step_ms_median": round(sorted(step_ms)[len(step_ms) // 2], 4),
+        "step_ms_min": round(min(step_ms), 4),
+        "kernels": per_kernel,
+        "roofline": roofline,
+        "input_setup_s": round(t_gen, 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = _ffn_cpu_baseline(x, w1, w2, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = _parse()
     if args.trace_overlap:
@@ -386,6 +504,9 @@ def main():
         return
     if args.decode:
         _bench_decode(args)
+        return
+    if args.ffn:
+        _bench_ffn(args)
         return
 
     import torch

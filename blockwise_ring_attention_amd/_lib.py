@@ -59,6 +59,7 @@ _SIGS = {
     "ring_attn_decode_chunk": ([ctypes.POINTER(Dims)], _i),
     "ring_attn_decode_splits": ([ctypes.POINTER(Dims), _i], _i),
     "ring_attn_fwd_decode": ([_vp, _vp, _i, _vp, _vp, _vp, _vp, ctypes.POINTER(Dims), _vp], _i),
+    "ring_ffn_fwd": ([_vp, _vp, _vp, _vp, _vp, ctypes.c_int64, _i, _i, _i, _vp], _i),
     "ring_attn_timing_enable": ([_i], _i),
     "ring_attn_timing_read": ([ctypes.c_char_p, ctypes.POINTER(_i), ctypes.POINTER(ctypes.c_double)], _i),
 }
@@ -189,6 +190,24 @@ def ring_attn_fwd_decode(q, kv_block, k_chunk, o_acc, lse_acc, o_part, lse_part,
     _check(load().ring_attn_fwd_decode(_ptr(q), _ptr(kv_block), int(k_chunk), _ptr(o_acc),
                                        _ptr(lse_acc), _ptr(o_part), _ptr(lse_part),
                                        ctypes.byref(dm), _stream(stream)))
+
+
+def ring_ffn_fwd(x, w1, w2, hidden, out, chunk_rows, stream=None):
+    """Blockwise feedforward out = GELU(x w1^T) w2^T over x [rows, d_model],
+    chunk_rows rows at a time through the caller's hidden [>= min(rows,
+    chunk_rows), d_ff] workspace; all bf16."""
+    for t, n in ((x, "x"), (w1, "w1"), (w2, "w2"), (hidden, "hidden"), (out, "out")):
+        _need(t, torch.bfloat16, n)
+    rows, d_model = x.shape
+    d_ff = w1.shape[0]
+    if tuple(w1.shape) != (d_ff, d_model) or tuple(w2.shape) != (d_model, d_ff):
+        raise ValueError("w1 must be [d_ff, d_model] and w2 [d_model, d_ff]")
+    if tuple(out.shape) != (rows, d_model):
+        raise ValueError("out must be [rows, d_model]")
+    if hidden.numel() < min(rows, max(int(chunk_rows), 1)) * d_ff:
+        raise ValueError("hidden holds fewer than min(rows, chunk_rows) x d_ff elements")
+    _check(load().ring_ffn_fwd(_ptr(x), _ptr(w1), _ptr(w2), _ptr(hidden), _ptr(out), rows,
+                               d_model, d_ff, int(chunk_rows), _stream(stream)))
 
 
 def ring_attn_combine(o_a, lse_a, o_b, lse_b, stream=None):

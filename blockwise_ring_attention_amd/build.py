@@ -22,7 +22,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libringattn.so")
 
 SOURCES = ["api.cpp", "emulator.cpp", "elementwise.hip", "fwd_fp32.hip",
-           "fwd_bf16.hip", "bwd_bf16.hip", "decode_bf16.hip"]
+           "fwd_bf16.hip", "bwd_bf16.hip", "decode_bf16.hip",
+           "ffn_bf16.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU instructions are disabled on purpose for every HIP source.

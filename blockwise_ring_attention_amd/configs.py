@@ -138,6 +138,29 @@ DECODE_CONFIGS: Dict[str, DecodeConfig] = {
 }
 
 
+@dataclass(frozen=True)
+class FfnConfig:
+    """The blockwise feedforward of a member's rows: ``rows`` tokens of width
+    ``d_model`` through a ``d_ff``-wide hidden layer, ``chunk_rows`` rows at a
+    time (Ring Attention with Blockwise Transformers, abstract: blockwise
+    feedforward).  x ~ N(0, 1); W1 ~ N(0, 1/d_model) and W2 ~ N(0, 1/d_ff),
+    so pre-activations and outputs are of order one."""
+    cfg_id: int
+    name: str
+    rows: int
+    d_model: int
+    d_ff: int
+    chunk_rows: int
+
+
+FFN_CONFIGS: Dict[str, FfnConfig] = {
+    # One member's 16384-token block of the 7B model (width 32 x 128 = 4096,
+    # hidden 4 x 4096), 4096 rows per chunk.
+    "ffn-lwm7b": FfnConfig(7, "ffn-lwm7b", rows=16384, d_model=4096, d_ff=16384,
+                           chunk_rows=4096),
+}
+
+
 def scaled(cfg: ShareConfig, **changes) -> ShareConfig:
     """A copy of ``cfg`` with some fields replaced (smaller parity cases)."""
     from dataclasses import replace

@@ -21,9 +21,11 @@ namespace {
 thread_local std::string g_last_error;
 
 // ---- kernel timing: event pairs around launches, kept until read ---------
-enum Kind { kFwdBf16 = 0, kFwdFp32, kBwdDq, kBwdDkv, kDecode, kDecodeFold, kKinds };
-const char* const kKindNames[kKinds] = {"fwd_bf16", "fwd_fp32",   "bwd_dq",
-                                        "bwd_dkv",  "fwd_decode", "decode_fold"};
+enum Kind {
+  kFwdBf16 = 0, kFwdFp32, kBwdDq, kBwdDkv, kDecode, kDecodeFold, kFfnUp, kFfnDown, kKinds
+};
+const char* const kKindNames[kKinds] = {"fwd_bf16",   "fwd_fp32",    "bwd_dq", "bwd_dkv",
+                                        "fwd_decode", "decode_fold", "ffn_up", "ffn_down"};
 
 struct TimingRec {
   int kind;
@@ -256,7 +258,7 @@ int ra_decode_splits(const ra_shape& s, int k_chunk) {
 
 extern "C" {
 
-int ring_attn_version(void) { return 201; }
+int ring_attn_version(void) { return 202; }
 
 int ring_attn_timing_enable(int on) {
   std::lock_guard<std::mutex> g(g_tmu);
@@ -453,6 +455,44 @@ int ring_attn_fwd_decode(const void* q, const void* kv_block, int k_chunk, float
   e = ra_launch_decode_fold(o_acc, lse_acc, o_part, lse_part, s.q_rows, s.D, S, L.stream);
   tf.done();
   return e == hipSuccess ? RA_OK : ra_hip_fail(e, "decode fold kernel launch");
+}
+
+int ring_ffn_fwd(const void* x, const void* w1, const void* w2, void* hidden, void* out,
+                 int64_t rows, int d_model, int d_ff, int chunk_rows, void* stream) {
+  if (rows < 0 || rows > 0x7fffffffLL)
+    return ra_fail(RA_ERR_INVALID, "rows %lld outside [0, 2^31)", (long long)rows);
+  if (d_model < 256 || d_ff < 256 || d_model % 256 != 0 || d_ff % 256 != 0)
+    return ra_fail(RA_ERR_UNSUPPORTED, "d_model %d and d_ff %d must be positive multiples of 256",
+                   d_model, d_ff);
+  if (chunk_rows < 1) return ra_fail(RA_ERR_INVALID, "chunk_rows %d must be >= 1", chunk_rows);
+  if (rows == 0) return RA_OK;
+  if (!x || !w1 || !w2 || !hidden || !out) return ra_fail(RA_ERR_INVALID, "NULL tensor pointer");
+  const int64_t chunk = std::min<int64_t>(chunk_rows, rows);
+  if (((chunk + 255) / 256) * (int64_t)(std::max(d_model, d_ff) / 256) > 0x7fffffffLL)
+    return ra_fail(RA_ERR_INVALID, "problem too large for one launch");
+  const size_t xb = (size_t)rows * d_model * 2, w1b = (size_t)d_ff * d_model * 2,
+               w2b = w1b, hb = (size_t)chunk * d_ff * 2, ob = xb;
+  const void* ins[3] = {x, w1, w2};
+  const size_t insz[3] = {xb, w1b, w2b};
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(hidden, hb, ins[i], insz[i]) || overlaps(out, ob, ins[i], insz[i]))
+      return ra_fail(RA_ERR_INVALID, "hidden / out overlap an input");
+  if (overlaps(hidden, hb, out, ob)) return ra_fail(RA_ERR_INVALID, "hidden overlaps out");
+  hipStream_t st = (hipStream_t)stream;
+  for (int64_t r0 = 0; r0 < rows; r0 += chunk) {
+    const int m = (int)std::min<int64_t>(chunk, rows - r0);
+    Timed tu(kFfnUp, st);
+    hipError_t e = ra_launch_ffn_up((const char*)x + (size_t)r0 * d_model * 2, w1, hidden, m,
+                                    d_model, d_ff, st);
+    tu.done();
+    if (e != hipSuccess) return ra_hip_fail(e, "feedforward up-projection launch");
+    Timed td(kFfnDown, st);
+    e = ra_launch_ffn_down(hidden, w2, (char*)out + (size_t)r0 * d_model * 2, m, d_model, d_ff,
+                           st);
+    td.done();
+    if (e != hipSuccess) return ra_hip_fail(e, "feedforward down-projection launch");
+  }
+  return RA_OK;
 }
 
 }  // extern "C"

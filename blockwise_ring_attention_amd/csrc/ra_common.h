@@ -385,6 +385,14 @@ hipError_t ra_launch_decode_split(const void* q, const void* kv, float* o_part, 
 hipError_t ra_launch_decode_fold(float* o_acc, float* lse_acc, const float* o_part,
                                  const float* lse_part, int64_t rows, int D, int splits,
                                  hipStream_t stream);
+// Blockwise feedforward products (bf16, fp32 accumulation):
+//   ffn_up:   hidden[r][f] = bf16(GELU(sum_c x[r][c] w1[f][c]))   rows x d_ff
+//   ffn_down: out[r][c]    = bf16(sum_f hidden[r][f] w2[c][f])    rows x d_model
+// d_model and d_ff multiples of 256, rows >= 1.
+hipError_t ra_launch_ffn_up(const void* x, const void* w1, void* hidden, int rows, int d_model,
+                            int d_ff, hipStream_t stream);
+hipError_t ra_launch_ffn_down(const void* hidden, const void* w2, void* out, int rows,
+                              int d_model, int d_ff, hipStream_t stream);
 hipError_t ra_launch_fwd_fp32(const float* q, const float* kv, float* o_acc,
                               float* lse_acc, const ra_launch& a);
 hipError_t ra_launch_init_acc(float* o_acc, float* lse_acc, int64_t rows,

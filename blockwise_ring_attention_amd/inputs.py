@@ -12,9 +12,9 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from .configs import DecodeConfig, ShareConfig
+from .configs import DecodeConfig, FfnConfig, ShareConfig
 
-TENSOR_ID = {"q": 0, "k": 1, "v": 2, "do": 3}
+TENSOR_ID = {"q": 0, "k": 1, "v": 2, "do": 3, "x": 4, "w1": 5, "w2": 6}
 
 
 def _rng(seed: int, cfg_id: int, tensor: str, block: int) -> np.random.Generator:
@@ -65,6 +65,20 @@ def draw_decode(cfg: DecodeConfig, seed: int = 0):
     packed key/value blocks [2, B, Hkv, Lk, d], in arrival order."""
     q = draw(cfg, "q", cfg.blocks, seed, length=cfg.q_len)
     return q, [draw_kv(cfg, i, seed) for i in range(cfg.blocks)]
+
+
+def draw_ffn(cfg: FfnConfig, seed: int = 0):
+    """Inputs of the blockwise feedforward, bf16 (RNE from float32):
+    x [rows, d_model] ~ N(0, 1), w1 [d_ff, d_model] ~ N(0, 1/d_model),
+    w2 [d_model, d_ff] ~ N(0, 1/d_ff)."""
+    out = []
+    for name, shape, std in (("x", (cfg.rows, cfg.d_model), 1.0),
+                             ("w1", (cfg.d_ff, cfg.d_model), cfg.d_model ** -0.5),
+                             ("w2", (cfg.d_model, cfg.d_ff), cfg.d_ff ** -0.5)):
+        a = _rng(seed, cfg.cfg_id, name, 0).standard_normal(shape, dtype=np.float32)
+        a *= np.float32(std)
+        out.append(torch.from_numpy(a).to(torch.bfloat16))
+    return tuple(out)
 
 
 def torch_dtype(cfg: ShareConfig | DecodeConfig) -> torch.dtype:

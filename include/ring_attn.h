@@ -185,6 +185,31 @@ int ring_attn_fwd_decode(const void* q, const void* kv_block, int k_chunk,
                          float* o_acc, float* lse_acc, float* o_part,
                          float* lse_part, const ra_dims* dims, void* stream);
 
+/* ---- blockwise feedforward ----------------------------------------------
+ * The method computes self-attention and the feedforward blockwise (Ring
+ * Attention with Blockwise Transformers, abstract; sourcepulse project page,
+ * How It Works: attention and feedforward are both distributed).  The
+ * feedforward is position-wise, so a member applies it to its own rows with
+ * no communication, chunk_rows rows at a time, and the hidden activation
+ * never exceeds [chunk_rows, d_ff].  The pages do not give its form; this is
+ * the position-wise two-layer MLP
+ *     out = GELU(x W1^T) W2^T,   GELU(z) = z/2 (1 + erf(z / sqrt 2)),
+ * with the hidden activation rounded to bf16 (RNE) before the second
+ * product and out rounded to bf16 (RNE); products accumulate in fp32.
+ *   x      [rows, d_model]  bf16 (device)
+ *   w1     [d_ff, d_model]  bf16 (out x in, the layout of a linear layer)
+ *   w2     [d_model, d_ff]  bf16
+ *   hidden [min(rows, chunk_rows), d_ff]  bf16 workspace owned by the caller;
+ *          its contents on return are unspecified
+ *   out    [rows, d_model]  bf16
+ * d_model and d_ff must be positive multiples of 256 (RA_ERR_UNSUPPORTED);
+ * chunk_rows >= 1 (RA_ERR_INVALID); hidden and out must not overlap each
+ * other or any input (RA_ERR_INVALID).  Each row's result is bitwise
+ * independent of chunk_rows.  rows == 0 does nothing. */
+int ring_ffn_fwd(const void* x, const void* w1, const void* w2, void* hidden,
+                 void* out, int64_t rows, int d_model, int d_ff, int chunk_rows,
+                 void* stream);
+
 /* ---- single-GPU ring emulator ------------------------------------------
  * Plays one member of a ring of ring_size members on one GPU.  The other
  * members' key/value blocks live in a device pool; the "hop" that would
@@ -234,7 +259,8 @@ int ring_emu_bwd(const void* q, const void* const* kv_pool, void* slot0,
  * While enabled, each attention kernel the library launches is bracketed by
  * a pair of HIP events recorded on the stream the kernel runs on.  Kernel
  * families: "fwd_bf16", "fwd_fp32", "bwd_dq", "bwd_dkv", "fwd_decode" (the
- * split kernel of ring_attn_fwd_decode) and "decode_fold" (its fold).
+ * split kernel of ring_attn_fwd_decode), "decode_fold" (its fold), and
+ * "ffn_up" / "ffn_down" (the two products of ring_ffn_fwd, per chunk).
  * ring_attn_timing_enable(on): on != 0 discards earlier records and starts
  * collecting; 0 stops collecting (records are kept).
  * ring_attn_timing_read(name, &launches, &total_ms): waits for the recorded

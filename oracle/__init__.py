@@ -15,6 +15,10 @@ What it computes
   Ring Attention with Blockwise Transformers, abstract), so the share of a
   ring member equals this definition restricted to the member's rows.
 * ``attention_grads``: the closed-form exact gradient of sum(dO * O).
+* ``ffn.feedforward``: the position-wise two-layer MLP GELU(x W1^T) W2^T
+  that the blockwise feedforward computes chunk by chunk (Ring Attention
+  with Blockwise Transformers, abstract: blockwise computation of
+  self-attention and feedforward; the form is a reading, the pages give none).
 * ``brute``: scalar triple loops with ``math.exp`` / ``math.fsum`` for tiny
   shapes.
 * ``ring``: a separate fp64 emulation of the ring schedule, the chunked online
@@ -29,7 +33,8 @@ fp64 autograd and SDPA as independent library routines, gradient sum
 identities, combine associativity / commutativity / identity.
 """
 from .exact import attention, attention_grads, positions
+from .ffn import feedforward, gelu
 from .ring import combine, block_partial, ring_share, ring_schedule
 
 __all__ = ["attention", "attention_grads", "positions", "combine",
-           "block_partial", "ring_share", "ring_schedule"]
+           "block_partial", "ring_share", "ring_schedule", "feedforward", "gelu"]

@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
     for n in ("ring_attn_fwd", "ring_attn_combine", "ring_attn_bwd", "ring_attn_bwd_prep",
               "ring_attn_finalize", "ring_attn_init_acc", "ring_attn_last_error",
               "ring_attn_version", "ring_emu_fwd", "ring_emu_bwd", "ring_attn_fwd_decode",
-              "ring_attn_decode_chunk", "ring_attn_decode_splits"):
+              "ring_attn_decode_chunk", "ring_attn_decode_splits", "ring_ffn_fwd"):
         assert n in names
     assert sorted(_lib.EXPORTS) == names, "binding and header disagree"
 
@@ -39,7 +39,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.ring_attn_version() == 201
+    assert lib.ring_attn_version() == 202
     assert lib.ring_attn_last_error() == b""
 
 
@@ -171,6 +171,33 @@ def test_decode_split_planning(lib):
         kc = chunk(**kw)
         assert kc > 0 and kc % 128 == 0
         assert splits(kc, **kw) <= 65536
+
+
+def _ffn(lib, rows=300, dm=256, dff=512, chunk=128, x=FAKE, w1=ctypes.c_void_p(0x1000000),
+         w2=ctypes.c_void_p(0x2000000), hidden=ctypes.c_void_p(0x10000000),
+         out=ctypes.c_void_p(0x20000000)):
+    return lib.ring_ffn_fwd(x, w1, w2, hidden, out, rows, dm, dff, chunk, None)
+
+
+def test_ffn_rejects_invalid_and_unsupported(lib):
+    assert _ffn(lib, dm=200) == -2                     # multiples of 256 only
+    assert _ffn(lib, dff=640) == -2
+    assert _ffn(lib, dm=0) == -2
+    assert _ffn(lib, rows=-1) == -1
+    assert _ffn(lib, rows=1 << 31) == -1
+    assert _ffn(lib, chunk=0) == -1
+    assert _ffn(lib, x=None) == -1
+    assert _ffn(lib, hidden=None) == -1
+    assert _ffn(lib, out=None) == -1
+    # x [300, 256] bf16 spans 150 KiB from 0x1000
+    assert _ffn(lib, out=ctypes.c_void_p(0x1000 + 4096)) == -1          # out overlaps x
+    assert _ffn(lib, hidden=ctypes.c_void_p(0x2000000 + 64)) == -1      # hidden overlaps w2
+    assert _ffn(lib, hidden=ctypes.c_void_p(0x20000000 - 1024)) == -1   # hidden overlaps out
+    assert b"multiples of 256" in (_ffn(lib, dm=96) and lib.ring_attn_last_error())
+
+
+def test_ffn_empty_is_a_no_op(lib):
+    assert _ffn(lib, rows=0, x=None, w1=None, w2=None, hidden=None, out=None) == 0
 
 
 def test_emulator_rejects_bad_schedules(lib):

@@ -1,0 +1,142 @@
+"""Pins of the blockwise-feedforward oracle (oracle/ffn.py) against facts fixed
+outside it: printed values of the normal distribution function, a scalar
+brute-force evaluation, torch's fp64 linear and GELU (library routines), and
+the identities of a position-wise map.  The last test plants slips in the
+oracle and checks that the pins catch them."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.ffn as of
+from oracle import feedforward, gelu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(rng, rows, d_model, d_ff):
+    return (rng.standard_normal((rows, d_model)),
+            rng.standard_normal((d_ff, d_model)) / math.sqrt(d_model),
+            rng.standard_normal((d_model, d_ff)) / math.sqrt(d_ff))
+
+
+def _pin_table(ffn=None):
+    """With W1 = W2 = identity, FFN(x) = GELU(x) = x Phi(x) elementwise."""
+    ffn = ffn or feedforward
+    g = json.load(open(os.path.join(GOLDEN, "ffn_gelu_table.json")))
+    z = np.array([float(k) for k in g["phi"]] + [-float(k) for k in g["phi"]])
+    phi = np.array(list(g["phi"].values()) + [1.0 - p for p in g["phi"].values()])
+    n = len(z)
+    got = ffn(z[None, :], np.eye(n), np.eye(n))[0]
+    return np.abs(got - z * phi).max() <= 1e-14
+
+
+def _brute(x, w1, w2):
+    out = []
+    for row in x:
+        h = []
+        for wf in w1:
+            a = math.fsum(xi * wi for xi, wi in zip(row, wf))
+            h.append(a * 0.5 * (1.0 + math.erf(a / math.sqrt(2.0))))
+        out.append([math.fsum(hf * w for hf, w in zip(h, wc)) for wc in w2])
+    return np.array(out)
+
+
+def _pin_brute(ffn=None):
+    ffn = ffn or feedforward
+    rng = np.random.default_rng(1)
+    x, w1, w2 = _rand(rng, 5, 4, 7)
+    return np.abs(ffn(x, w1, w2) - _brute(x.tolist(), w1.tolist(), w2.tolist())).max() <= 1e-13
+
+
+def _pin_torch(ffn=None, d_model=16, d_ff=40):
+    ffn = ffn or feedforward
+    rng = np.random.default_rng(2)
+    x, w1, w2 = _rand(rng, 33, d_model, d_ff)
+    t = [torch.from_numpy(a) for a in (x, w1, w2)]
+    ref = torch.nn.functional.linear(
+        torch.nn.functional.gelu(torch.nn.functional.linear(t[0], t[1]), approximate="none"), t[2])
+    return np.abs(ffn(x, w1, w2) - ref.numpy()).max() <= 1e-12
+
+
+def test_gelu_matches_the_normal_table():
+    assert _pin_table()
+
+
+def test_gelu_special_values():
+    assert gelu(0.0) == 0.0
+    assert abs(gelu(40.0) - 40.0) < 1e-12          # Phi -> 1
+    assert abs(gelu(-40.0)) < 1e-12                # Phi -> 0
+
+
+def test_brute_force_tiny():
+    assert _pin_brute()
+
+
+def test_library_torch_fp64():
+    assert _pin_torch()
+
+
+def test_position_wise_and_blockwise():
+    """Rows are independent: permuting rows permutes outputs, and chunks of
+    rows evaluated separately give the same rows (the blockwise form)."""
+    rng = np.random.default_rng(3)
+    x, w1, w2 = _rand(rng, 50, 8, 24)
+    full = feedforward(x, w1, w2)
+    perm = rng.permutation(50)
+    np.testing.assert_array_equal(feedforward(x[perm], w1, w2), full[perm])
+    chunks = np.concatenate([feedforward(x[i:i + 16], w1, w2) for i in range(0, 50, 16)])
+    np.testing.assert_array_equal(chunks, full)
+
+
+def test_linear_in_w2():
+    rng = np.random.default_rng(4)
+    x, w1, w2 = _rand(rng, 9, 8, 12)
+    w2b = rng.standard_normal(w2.shape)
+    lhs = feedforward(x, w1, 2.0 * w2 - 0.5 * w2b)
+    rhs = 2.0 * feedforward(x, w1, w2) - 0.5 * feedforward(x, w1, w2b)
+    np.testing.assert_allclose(lhs, rhs, atol=1e-12, rtol=0)
+
+
+def test_shape_mismatch_rejected():
+    with pytest.raises(ValueError):
+        feedforward(np.zeros((2, 4)), np.zeros((6, 4)), np.zeros((6, 4)))
+
+
+def _tanh_gelu(z):
+    z = np.asarray(z, dtype=np.float64)
+    return 0.5 * z * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (z + 0.044715 * z ** 3)))
+
+
+def _relu(z):
+    return np.maximum(np.asarray(z, dtype=np.float64), 0.0)
+
+
+_real_gelu = of.gelu
+
+
+def _sign_slip(z):
+    return _real_gelu(-np.asarray(z, dtype=np.float64))
+
+
+@pytest.mark.parametrize("slip", [_tanh_gelu, _relu, _sign_slip], ids=["tanh-form", "relu",
+                                                                      "sign"])
+def test_planted_activation_slip_is_caught(monkeypatch, slip):
+    assert _pin_table() and _pin_brute() and _pin_torch()
+    monkeypatch.setattr(of, "gelu", slip)
+    assert not (_pin_table() and _pin_brute() and _pin_torch())
+
+
+@pytest.mark.parametrize("which", ["w1", "w2"])
+def test_planted_untransposed_weight_is_caught(which):
+    """A weight used in the (in, out) instead of the (out, in) layout: with
+    square weights the shapes still chain, so only the values can tell."""
+    def slipped(x, w1, w2):
+        x, w1, w2 = of._as64(x), of._as64(w1), of._as64(w2)
+        a = x @ (w1 if which == "w1" else w1.T)
+        return of.gelu(a) @ (w2 if which == "w2" else w2.T)
+    assert _pin_torch(d_model=16, d_ff=16)
+    assert not _pin_torch(slipped, d_model=16, d_ff=16)
