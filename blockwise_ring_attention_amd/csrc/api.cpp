@@ -13,7 +13,7 @@
 #include <vector>
 
 #include "ra_api_internal.h"
-#include "ra_common.h"
+#include "ra_launch.h"
 #include "ring_attn.h"
 
 namespace {

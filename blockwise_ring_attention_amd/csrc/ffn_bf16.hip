@@ -16,8 +16,9 @@
 // four waves of 128 x 128 (one wave per SIMD; the accumulators take 256
 // registers), K in steps of 64 staged through two LDS stages of
 // 2 x 256 x 64 bf16 filled by direct-to-LDS copies one step ahead.  Tiles
-// are ordered in groups of four row tiles per XCD so that the workgroups
-// running together on one XCD share A and B tiles in its L2.
+// are ordered in groups of eight row tiles per XCD so that the workgroups
+// running together on one XCD share A and B tiles in its L2.  The epilogue
+// stages the output tile in LDS and stores it with 16-byte writes.
 #include <math.h>
 
 #include "ra_common.h"
@@ -26,65 +27,128 @@ using namespace ra;
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int ROWB = BK * 2;                 // bytes per staged row
-constexpr int TILEB = BM * ROWB;             // one staged A (or B) tile, 32 KiB
-constexpr int STAGEB = 2 * TILEB;            // A then B
-constexpr int GROUP_M = 4;                   // row tiles per group in the tile order
+constexpr int BM = 256, BN = 256;
+constexpr int GROUP_M = 8;                   // row tiles per group in the tile order
+// Output tile staged in LDS for the epilogue: 256 rows of 256 bf16, padded
+// to 528 bytes so that the 8-byte writes of 32 consecutive rows spread over
+// the banks and every 16-byte read stays aligned.
+constexpr int OUT_ROWB = BN * 2 + 16;
 
-// Copies rows [r0, r0 + 256) x columns [k0, k0 + 64) of a row-major
-// [rows x ld] bf16 matrix into a swizzled [256 x 64] LDS tile: 16-byte chunk c
-// of tile row r sits at physical chunk c ^ swz<64>(r).  Copy j (1 KiB) fills
-// tile rows 8j .. 8j + 7; lane l writes physical chunk l & 7 of row
-// 8j + (l >> 3), so it fetches logical chunk (l & 7) ^ swz<64>(8j + (l >> 3)).
-// swz<64>(8j + r) = swz<64>(r) ^ 2 (j & 1) for r < 8, and ld is a multiple of
-// 64 elements, so the lane offset for odd j is the even one with bit 5
-// flipped.  Rows at or past `rows` are clamped to rows - 1 (their products
-// are never stored).  Each wave issues copies j = 8 w .. 8 w + 7.
+// Staging of K steps of BK columns (32 or 64) in NSTAGE LDS stages, each an
+// A tile and a B tile of 256 rows x BK bf16.
+template <int BK, int NSTAGE>
+struct GemmCfg {
+  static constexpr int ROWB = BK * 2;               // bytes per staged row
+  static constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
+  static constexpr int RPL = 1024 / ROWB;           // rows per 1 KiB copy
+  static constexpr int LPW = BM / RPL / 4;          // copies per wave per tile
+  static constexpr int TILEB = BM * ROWB;
+  static constexpr int STAGEB = 2 * TILEB;          // A then B
+  static constexpr int SMEM = NSTAGE * STAGEB > BM * OUT_ROWB ? NSTAGE * STAGEB : BM * OUT_ROWB;
+  static constexpr int DS = BK / 16;                // 16-wide MFMA slices per step
+};
+
+// Physical 16-byte chunk of logical chunk c in staged row r is c ^ gswz(r):
+// 64-column rows use the attention tiles' swizzle, 32-column rows (four
+// chunks) XOR with bits 2-3 of the row.  Either way the 16-byte reads of 32
+// consecutive rows at one logical chunk hit distinct banks.
+template <int BK>
+__device__ __forceinline__ int gswz(int r) {
+  if constexpr (BK == 64)
+    return swz<64>(r);
+  else
+    return (r >> 2) & 3;
+}
+
+// Copies rows [r0, r0 + 256) x columns [k0, k0 + BK) of a row-major
+// [rows x ld] bf16 matrix into a swizzled LDS tile.  Copy j (1 KiB) fills
+// tile rows RPL j .. RPL j + RPL - 1; lane l writes physical chunk l % CPR of
+// row RPL j + l / CPR, so it fetches logical chunk
+// (l % CPR) ^ gswz(RPL j + l / CPR) = (l % CPR) ^ gswz(l / CPR) ^ gswz(RPL j)
+// (the swizzles are XOR-linear over these row bits; gswz(RPL j) is 2 (j & 1)
+// for 64 columns and 0 for 32).  ld is a multiple of 64 elements, so that XOR
+// never reaches the row part of the offset.  Rows at or past `rows` are
+// clamped to rows - 1 (their products are never stored).  Wave w issues
+// copies LPW w .. LPW w + LPW - 1.
+template <int BK, int NSTAGE>
 struct StridedTileLoader {
-  uint32_t voff;    // lane byte offset for even j (row part + chunk)
-  int lane_row;     // l >> 3
-  int lane_chunk;   // logical chunk for even j
+  using C = GemmCfg<BK, NSTAGE>;
+  uint32_t voff;    // lane byte offset for j with gswz(RPL j) = 0
+  int lane_row;
+  int lane_chunk;   // logical chunk for those j
   int wave;
   __device__ __forceinline__ StridedTileLoader(int wave_, int lane, int ld)
       : wave(__builtin_amdgcn_readfirstlane(wave_)) {
-    lane_row = lane >> 3;
-    lane_chunk = (lane & 7) ^ swz<64>(lane_row);
+    lane_row = lane / C::CPR;
+    lane_chunk = (lane % C::CPR) ^ gswz<BK>(lane_row);
     voff = (uint32_t)(lane_row * ld * 2 + lane_chunk * 16);
   }
   __device__ __forceinline__ void issue(uint32_t tile_lds, const bf16* src, int r0, int rows,
                                         int ld, int k0) const {
-    if (r0 + 256 <= rows) {  // whole tile in range: scalar row base per copy
+    if (r0 + BM <= rows) {  // whole tile in range: scalar row base per copy
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int j = wave * 8 + i;
+      for (int i = 0; i < C::LPW; ++i) {
+        const int j = wave * C::LPW + i;
         const uint32_t lds = __builtin_amdgcn_readfirstlane(tile_lds + (uint32_t)j * 1024);
-        const uint32_t v[1] = {voff ^ (uint32_t)((j & 1) << 5)};
-        dma16_group<1>(uniform(src + (size_t)(r0 + 8 * j) * ld + k0), v, lds);
+        const uint32_t v[1] = {voff ^ (uint32_t)(gswz<BK>(C::RPL * j) << 4)};
+        dma16_group<1>(uniform(src + (size_t)(r0 + C::RPL * j) * ld + k0), v, lds);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int j = wave * 8 + i;
+      for (int i = 0; i < C::LPW; ++i) {
+        const int j = wave * C::LPW + i;
         const uint32_t lds = __builtin_amdgcn_readfirstlane(tile_lds + (uint32_t)j * 1024);
-        const int row = min(r0 + 8 * j + lane_row, rows - 1);
-        const int chunk = lane_chunk ^ ((j & 1) << 1);
+        const int row = min(r0 + C::RPL * j + lane_row, rows - 1);
+        const int chunk = lane_chunk ^ gswz<BK>(C::RPL * j);
         dma16(src + (size_t)row * ld + k0 + chunk * 8, lds);
       }
     }
   }
 };
 
+// Waits until at most `pending` (0 .. K) steps of LPT copies each are still
+// in flight for this wave (copies complete in issue order).
+template <int LPT, int K>
+__device__ __forceinline__ void wait_steps_pending(int pending) {
+  if constexpr (K == 0) {
+    wait_vmem();
+  } else {
+    if (pending >= K)
+      wait_vmem_n<K * LPT>();
+    else
+      wait_steps_pending<LPT, K - 1>(pending);
+  }
+}
+
+// GELU(z) = z Phi(z) with Phi(z) = erfc(-z / sqrt 2) / 2.  erfc(u) for u >= 0
+// from the rational approximation of Abramowitz and Stegun, Handbook of
+// Mathematical Functions, formula 7.1.26 (|error of erf| <= 1.5e-7):
+//   erfc(u) ~ (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-u^2),
+//   t = 1 / (1 + p u).
+// Phi(z) = 1 - erfc(|z|/sqrt 2)/2 for z >= 0 and erfc(|z|/sqrt 2)/2 for
+// z < 0, so no 1 - erf cancellation is formed.  In fp32 with the hardware
+// exp2 and reciprocal, |GELU error| < 5e-7 (checked against the exact form),
+// well below the bf16 rounding of the hidden activation that follows.
 __device__ __forceinline__ float gelu(float z) {
-  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+  constexpr float p = 0.3275911f, a1 = 0.254829592f, a2 = -0.284496736f, a3 = 1.421413741f,
+                  a4 = -1.453152027f, a5 = 1.061405429f;
+  const float u = fabsf(z) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(p, u, 1.0f));
+  const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, a5, a4), a3), a2), a1);
+  const float ec = poly * exp2_fast(-u * u * kLog2e);
+  return z * (z >= 0.0f ? fmaf(-0.5f, ec, 1.0f) : 0.5f * ec);
 }
 
 // C[m][n] = epi(sum_k A[m][k] B[n][k]) for m < M; N % 256 == 0, K % 64 == 0.
-template <bool GELU>
+template <bool GELU, int BK, int NSTAGE>
 __global__ __launch_bounds__(256, 1) void gemm_tn_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ B, bf16* __restrict__ C, int M,
     int N, int K, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGEB];
+  using G = GemmCfg<BK, NSTAGE>;
+  constexpr int ROWB = G::ROWB, DS = G::DS, PF = NSTAGE - 1;
+  constexpr int LPT = 2 * G::LPW;   // this wave's copies per step (A and B)
+  static_assert((PF - 1) * LPT < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char smem[G::SMEM];
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lvoid*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -103,13 +167,17 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_kernel(
   const int m0 = tm * BM, n0 = tn * BN;
   const int wm = wave >> 1, wn = wave & 1;   // the wave's 128 x 128 quadrant
 
-  const StridedTileLoader loader(wave, lane, K);
+  const StridedTileLoader<BK, NSTAGE> loader(wave, lane, K);
   auto issue = [&](int kt) __attribute__((always_inline)) {
-    const uint32_t st = smem_lds + (kt & 1) * STAGEB;
+    const uint32_t st = smem_lds + (kt % NSTAGE) * G::STAGEB;
     loader.issue(st, A, m0, M, K, kt * BK);
-    loader.issue(st + TILEB, B, n0, N, K, kt * BK);
+    loader.issue(st + G::TILEB, B, n0, N, K, kt * BK);
   };
-  const LdsOffsets<64> off(lane);
+  // Per-lane offsets of the 16-byte MFMA operand reads: row l32 of a 32-row
+  // block, logical chunk 2 ds + hl.
+  int roff[DS];
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) roff[ds] = l32 * ROWB + (((2 * ds + hl) ^ gswz<BK>(l32)) << 4);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -119,20 +187,24 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_kernel(
 
   // Fragments of one 16-wide K slice: a[i] rows 32 i .. of the wave's A
   // quadrant, b[j] rows 32 j .. of its B quadrant; two sets, so the reads of
-  // slice ds + 1 run under the MFMAs of slice ds.
+  // the next slice run under the MFMAs of this one.
   bf16x8 fa[2][4], fb[2][4];
   auto read = [&](int set, int stage, int ds) __attribute__((always_inline)) {
-    const char* As = smem + stage * STAGEB + wm * 128 * ROWB + off.row[ds];
-    const char* Bs = smem + stage * STAGEB + TILEB + wn * 128 * ROWB + off.row[ds];
+    const char* As = smem + stage * G::STAGEB + wm * 128 * ROWB + roff[ds];
+    const char* Bs = smem + stage * G::STAGEB + G::TILEB + wn * 128 * ROWB + roff[ds];
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[set][i] = *(const bf16x8*)(As + i * 32 * ROWB);
 #pragma unroll
     for (int j = 0; j < 4; ++j) fb[set][j] = *(const bf16x8*)(Bs + j * 32 * ROWB);
   };
+  // B fragments as the MFMA's first operand: lane l32 of acc[i][j] holds row
+  // 32 i + l32 of the quadrant, register r its column 32 j + 8 (r / 4) +
+  // 4 (lane / 32) + r % 4, so four consecutive registers are four adjacent
+  // columns of one row.
   auto mfmas = [&](int set, int first, int count) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = first; q < first + count; ++q)
-      acc[q >> 2][q & 3] = mfma32(fa[set][q >> 2], fb[set][q & 3], acc[q >> 2][q & 3]);
+      acc[q >> 2][q & 3] = mfma32(fb[set][q & 3], fa[set][q >> 2], acc[q >> 2][q & 3]);
   };
   // One MFMA, then one LDS read, eight times; then the remaining MFMAs.
   auto interleave8 = [&]() __attribute__((always_inline)) {
@@ -144,65 +216,87 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_kernel(
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   };
 
+  // Steps 0 .. PF-1 before the loop; step kt issues step kt + PF into the
+  // stage of step kt - 1 (last read in iteration kt - 1, before the barrier
+  // in its last slice).  The copies go out together at the top of the step:
+  // spreading them between the MFMAs measured slower.
   const int nk = K / BK;
-  issue(0);
-  wait_vmem();
+#pragma unroll
+  for (int s = 0; s < PF; ++s)
+    if (s < nk) issue(s);
+  wait_steps_pending<LPT, PF - 1>(min(nk, PF) - 1);
   __syncthreads();
   read(0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
-    const int stage = kt & 1;
-    // Stage (kt+1)&1 was last read in iteration kt-1, before the barrier in
-    // its last slice; the reads since then are of stage kt&1.
-    if (kt + 1 < nk) issue(kt + 1);
+    const int stage = kt % NSTAGE;
+    if (kt + PF < nk) issue(kt + PF);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ds = 0; ds < 3; ++ds) {
+    for (int ds = 0; ds + 1 < DS; ++ds) {
       read((ds + 1) & 1, stage, ds + 1);
       mfmas(ds & 1, 0, 16);
       interleave8();
       __builtin_amdgcn_sched_barrier(0);
     }
-    // Slice 3: half of its MFMAs, then (if a step follows) the wait for the
-    // next stage's copies, the barrier, and the next step's slice-0 reads
-    // under the other half.
-    mfmas(1, 0, 8);
+    // Last slice: half of its MFMAs, then (if a step follows) the wait for
+    // the next step's copies, the barrier, and the next step's first-slice
+    // reads under the other half.
+    constexpr int last = (DS - 1) & 1;
+    mfmas(last, 0, 8);
     __builtin_amdgcn_sched_barrier(0);
     if (kt + 1 < nk) {
-      wait_vmem();  // this wave's copies of step kt+1 have landed
+      // step kt+1 has landed; steps kt+2 .. kt+PF may stay in flight
+      wait_steps_pending<LPT, PF - 1>(min(nk, kt + PF + 1) - kt - 2);
       __syncthreads();
-      read(0, stage ^ 1, 0);
+      read(last ^ 1, (kt + 1) % NSTAGE, 0);
     }
-    mfmas(1, 8, 8);
+    mfmas(last, 8, 8);
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // Lane l32 holds column n of 16 rows per accumulator: each store writes 32
-  // consecutive columns of one row.
+  // Epilogue: each wave writes its quadrant (after the activation, as bf16)
+  // into the LDS tile, four adjacent columns per 8-byte write; then the
+  // workgroup stores the tile row by row, 16 bytes per lane.
+  __syncthreads();  // every wave is done reading the last stage
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn * 128 + j * 32 + l32;
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-        float v = acc[i][j][r];
-        if constexpr (GELU) v = gelu(v);
-        if (m < M) C[(size_t)m * N + n] = (bf16)v;
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x = acc[i][j][4 * g + e];
+          if constexpr (GELU) x = gelu(x);
+          v[e] = (bf16)x;
+        }
+        const int row = wm * 128 + i * 32 + l32;
+        const int col = wn * 128 + j * 32 + 8 * g + 4 * hl;
+        *(bf16x4*)(smem + row * OUT_ROWB + col * 2) = v;
       }
-    }
+  __syncthreads();
+#pragma unroll 4
+  for (int it = 0; it < BM * BN / 8 / 256; ++it) {
+    const int id = it * 256 + tid;
+    const int row = id >> 5, c = id & 31;   // 32 chunks of 8 columns per row
+    const u32x4 v = *(const u32x4*)(smem + row * OUT_ROWB + c * 16);
+    if (m0 + row < M) *(u32x4*)(C + (size_t)(m0 + row) * N + n0 + c * 8) = v;
+  }
 }
+
+constexpr int kBK = 64, kStages = 2;
 
 hipError_t gemm_tn(const bf16* A, const bf16* B, bf16* C, int M, int N, int K, bool gelu_epi,
                    hipStream_t stream) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
   const dim3 grid((unsigned)(tiles_m * tiles_n)), block(256);
   if (gelu_epi)
-    hipLaunchKernelGGL(gemm_tn_kernel<true>, grid, block, 0, stream, A, B, C, M, N, K, tiles_m,
-                       tiles_n);
+    hipLaunchKernelGGL((gemm_tn_kernel<true, kBK, kStages>), grid, block, 0, stream, A, B, C, M,
+                       N, K, tiles_m, tiles_n);
   else
-    hipLaunchKernelGGL(gemm_tn_kernel<false>, grid, block, 0, stream, A, B, C, M, N, K, tiles_m,
-                       tiles_n);
+    hipLaunchKernelGGL((gemm_tn_kernel<false, kBK, kStages>), grid, block, 0, stream, A, B, C,
+                       M, N, K, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -210,14 +304,14 @@ hipError_t gemm_tn(const bf16* A, const bf16* B, bf16* C, int M, int N, int K, b
 
 hipError_t ra_launch_ffn_up(const void* x, const void* w1, void* hidden, int rows, int d_model,
                             int d_ff, hipStream_t stream) {
-  if (rows < 1 || d_model % BK != 0 || d_ff % BN != 0) return hipErrorInvalidValue;
+  if (rows < 1 || d_model % 64 != 0 || d_ff % BN != 0) return hipErrorInvalidValue;
   return gemm_tn((const bf16*)x, (const bf16*)w1, (bf16*)hidden, rows, d_ff, d_model, true,
                  stream);
 }
 
 hipError_t ra_launch_ffn_down(const void* hidden, const void* w2, void* out, int rows,
                               int d_model, int d_ff, hipStream_t stream) {
-  if (rows < 1 || d_ff % BK != 0 || d_model % BN != 0) return hipErrorInvalidValue;
+  if (rows < 1 || d_ff % 64 != 0 || d_model % BN != 0) return hipErrorInvalidValue;
   return gemm_tn((const bf16*)hidden, (const bf16*)w2, (bf16*)out, rows, d_model, d_ff, false,
                  stream);
 }
