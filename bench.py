@@ -20,9 +20,11 @@ against one member's 16384-token share of the key/value cache.  That step
 streams the key/value block from HBM once, so it reports HBM GB/s of its
 algorithmic bytes against the 8 TB/s peak.
 
-``--ffn`` times the blockwise feedforward of one member's 16384-token block
-of the 7B model instead (width 4096, hidden 16384, 4096 rows per chunk):
-4·rows·d_model·d_ff flops in two bf16 MFMA products per chunk.
+``--ffn`` times a training step of the blockwise feedforward of one member's
+16384-token block of the 7B model instead (width 4096, hidden 16384, 4096
+rows per chunk): forward 4·rows·d_model·d_ff flops (two bf16 MFMA products
+per chunk) and backward 10·rows·d_model·d_ff (the up-projection recomputed,
+then dH, dx, dW1, dW2), weight gradients accumulating over the steps.
 
 Prints one JSON line.  ``--gpus`` above 1 is refused: this benchmark runs one
 member's share on one GPU.
@@ -380,22 +382,27 @@ def _bench_decode(args):
 FFN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ffn_lwm7b.json")
 
 
-def _ffn_cpu_baseline(x, w1, w2, target_s):
-    """The fp64 oracle, as it stands, on a bounded sample of the rows."""
+def _ffn_cpu_baseline(x, w1, w2, dout, target_s):
+    """The fp64 oracle, as it stands, forward and gradients on a bounded
+    sample of the rows (the first n rows, n growing until about target_s)."""
     import oracle
 
-    n, t0 = 8, time.perf_counter()
-    while True:
+    def run(n):
+        t0 = time.perf_counter()
         oracle.feedforward(x[:n], w1, w2)
-        dt = time.perf_counter() - t0
-        if dt > target_s / 4 or n >= x.shape[0]:
-            break
-        n, t0 = min(x.shape[0], n * 4), time.perf_counter()
-    flops = 4.0 * n * w1.shape[1] * w1.shape[0]
+        oracle.feedforward_grads(x[:n], w1, w2, dout[:n])
+        return time.perf_counter() - t0
+
+    n = 8
+    dt = run(n)
+    while dt < target_s / 4 and n < x.shape[0]:
+        n = min(x.shape[0], n * 4)
+        dt = run(n)
+    flops = 14.0 * n * w1.shape[1] * w1.shape[0]
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(_oracle_threads()),
             "kind": "oracle", "cpu_model": _cpu_model(),
-            "sample": (f"fp64 oracle feedforward of the first {n} of {x.shape[0]} rows "
-                       f"(d_model {w1.shape[1]}, d_ff {w1.shape[0]}), {dt:.1f} s"),
+            "sample": (f"fp64 oracle feedforward and gradients of the first {n} of {x.shape[0]} "
+                       f"rows (d_model {w1.shape[1]}, d_ff {w1.shape[0]}), {dt:.1f} s"),
             "seconds": round(dt, 2)}
 
 
@@ -404,61 +411,95 @@ def _bench_ffn(args):
 
     from blockwise_ring_attention_amd import _lib
     from blockwise_ring_attention_amd.configs import FFN_CONFIGS
-    from blockwise_ring_attention_amd.inputs import draw_ffn
+    from blockwise_ring_attention_amd.inputs import draw_ffn, draw_ffn_dout
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     _lib.load()
     cfg = FFN_CONFIGS["ffn-lwm7b"]
     t_gen = time.perf_counter()
     x, w1, w2 = draw_ffn(cfg, seed=0)
+    dout = draw_ffn_dout(cfg, seed=0)
     dev = torch.device("cuda:0")
-    xd, w1d, w2d = x.to(dev), w1.to(dev), w2.to(dev)
+    xd, w1d, w2d, dd = x.to(dev), w1.to(dev), w2.to(dev), dout.to(dev)
     hidden = torch.empty((min(cfg.rows, cfg.chunk_rows), cfg.d_ff), dtype=torch.bfloat16,
                          device=dev)
     out = torch.empty((cfg.rows, cfg.d_model), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty_like(xd)
+    dw1 = torch.zeros((cfg.d_ff, cfg.d_model), dtype=torch.float32, device=dev)
+    dw2 = torch.zeros((cfg.d_model, cfg.d_ff), dtype=torch.float32, device=dev)
+    work = torch.empty(_lib.ring_ffn_bwd_workspace(cfg.rows, cfg.d_model, cfg.d_ff,
+                                                   cfg.chunk_rows), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t_gen
     main_stream = torch.cuda.current_stream()
 
-    def step():
+    def fwd():
         _lib.ring_ffn_fwd(xd, w1d, w2d, hidden, out, cfg.chunk_rows)
+
+    def bwd():
+        _lib.ring_ffn_bwd(xd, w1d, w2d, dd, dx, dw1, dw2, work, cfg.chunk_rows)
+
+    def step():
+        fwd()
+        bwd()
+
+    def timed(fn, steps, per_step=None):
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        w0 = time.perf_counter()
+        ev[0].record(main_stream)
+        for i in range(steps):
+            fn()
+            ev[i + 1].record(main_stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - w0) * 1e3 / steps
+        if per_step is not None:
+            per_step.extend(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+        return ev[0].elapsed_time(ev[steps]) / steps, wall
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
     _lib.ring_attn_timing_enable(True)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    w0 = time.perf_counter()
-    ev[0].record(main_stream)
-    for i in range(args.steps):
-        step()
-        ev[i + 1].record(main_stream)
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - w0) * 1e3 / args.steps
+    step_ms = []
+    ms_step, wall = timed(step, args.steps, step_ms)
     _lib.ring_attn_timing_enable(False)
-    ms_step = ev[0].elapsed_time(ev[args.steps]) / args.steps
-    step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
     chunks = (cfg.rows + cfg.chunk_rows - 1) // cfg.chunk_rows
-    flops = 4.0 * cfg.rows * cfg.d_model * cfg.d_ff
-    tflops = flops / (ms_step * 1e-3) / 1e12
+    unit = 2.0 * cfg.rows * cfg.d_model * cfg.d_ff     # one product over all rows
+    fwd_flops, bwd_flops = 2 * unit, 5 * unit
+    tflops = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
+    # flops per step of each timed family (the backward's products in total)
+    fam_flops = {"ffn_up": unit, "ffn_down": unit, "ffn_bwd_gemm": 5 * unit}
     per_kernel = {}
-    for fam in ("ffn_up", "ffn_down"):
+    for fam in ("ffn_up", "ffn_down", "ffn_bwd_gemm", "ffn_bwd_aux"):
         n, tot = _lib.ring_attn_timing_read(fam)
         if n == 0:
             continue
-        avg = tot / n
-        fl = flops / 2 / chunks            # each product is half the flops, per chunk
-        per_kernel[fam] = {"launches": n, "avg_ms": round(avg, 4),
-                           "flops_per_launch": fl,
-                           "tflops": round(fl / (avg * 1e-3) / 1e12, 1),
-                           "frac": round(fl / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-    dom = max(per_kernel, key=lambda f: per_kernel[f]["avg_ms"] * per_kernel[f]["launches"])
+        rec = {"launch_groups": n, "total_ms_per_step": round(tot / args.steps, 4)}
+        if fam in fam_flops:
+            tf = fam_flops[fam] * args.steps / (tot * 1e-3) / 1e12
+            rec.update({"tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+            if fam in ("ffn_up", "ffn_down"):
+                rec["avg_ms"] = round(tot / n, 4)
+                rec["flops_per_launch"] = unit / chunks
+        per_kernel[fam] = rec
+    phases = {}
+    if not args.no_phases:
+        ms_f, _ = timed(fwd, args.steps)
+        ms_b, _ = timed(bwd, args.steps)
+        for name, ms, fl in (("fwd", ms_f, fwd_flops), ("bwd", ms_b, bwd_flops)):
+            tf = fl / (ms * 1e-3) / 1e12
+            phases[name] = {"ms": round(ms, 3), "tflops": round(tf, 1),
+                            "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    flops_fams = [f for f in per_kernel if "tflops" in per_kernel[f]]
+    dom = max(flops_fams, key=lambda f: per_kernel[f]["total_ms_per_step"])
     roofline = {"bound": "mfma", "achieved": per_kernel[dom]["tflops"], "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": per_kernel[dom]["frac"],
-                "traffic": _measured_traffic(dom, FFN_TRAFFIC_FILE),
+                "traffic": (_measured_traffic(dom, FFN_TRAFFIC_FILE)
+                            if dom in ("ffn_up", "ffn_down") else None),
                 "traffic_unit": "HBM bytes per launch", "kernel": dom}
     result = {
-        "metric": "blockwise feedforward TFLOP/s (4·rows·d_model·d_ff per pass); % of bf16 MFMA peak",
+        "metric": ("blockwise feedforward training-step TFLOP/s (fwd 4 + bwd 10 "
+                   "·rows·d_model·d_ff); % of bf16 MFMA peak"),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -470,20 +511,21 @@ def _bench_ffn(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": (f"ffn-lwm7b: {cfg.rows} rows, d_model {cfg.d_model}, d_ff {cfg.d_ff}, "
-                                f"GELU, {cfg.chunk_rows} rows per chunk"),
+        "config": {"workload": (f"ffn-lwm7b fwd+bwd: {cfg.rows} rows, d_model {cfg.d_model}, "
+                                f"d_ff {cfg.d_ff}, GELU, {cfg.chunk_rows} rows per chunk"),
                    "rows": cfg.rows, "d_model": cfg.d_model, "d_ff": cfg.d_ff,
                    "chunk_rows": cfg.chunk_rows},
         "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "wall_ms_per_step": round(wall, 4),
         "step_ms_median": round(sorted(step_ms)[len(step_ms) // 2], 4),
         "step_ms_min": round(min(step_ms), 4),
+        "phases": phases,
         "kernels": per_kernel,
         "roofline": roofline,
         "input_setup_s": round(t_gen, 1),
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = _ffn_cpu_baseline(x, w1, w2, args.cpu_seconds)
+        result["cpu_baseline"] = _ffn_cpu_baseline(x, w1, w2, dout, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

@@ -60,6 +60,9 @@ _SIGS = {
     "ring_attn_decode_splits": ([ctypes.POINTER(Dims), _i], _i),
     "ring_attn_fwd_decode": ([_vp, _vp, _i, _vp, _vp, _vp, _vp, ctypes.POINTER(Dims), _vp], _i),
     "ring_ffn_fwd": ([_vp, _vp, _vp, _vp, _vp, ctypes.c_int64, _i, _i, _i, _vp], _i),
+    "ring_ffn_bwd_workspace": ([ctypes.c_int64, _i, _i, _i], ctypes.c_int64),
+    "ring_ffn_bwd": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64, ctypes.c_int64, _i, _i,
+                      _i, _vp], _i),
     "ring_attn_timing_enable": ([_i], _i),
     "ring_attn_timing_read": ([ctypes.c_char_p, ctypes.POINTER(_i), ctypes.POINTER(ctypes.c_double)], _i),
 }
@@ -208,6 +211,35 @@ def ring_ffn_fwd(x, w1, w2, hidden, out, chunk_rows, stream=None):
         raise ValueError("hidden holds fewer than min(rows, chunk_rows) x d_ff elements")
     _check(load().ring_ffn_fwd(_ptr(x), _ptr(w1), _ptr(w2), _ptr(hidden), _ptr(out), rows,
                                d_model, d_ff, int(chunk_rows), _stream(stream)))
+
+
+def ring_ffn_bwd_workspace(rows, d_model, d_ff, chunk_rows) -> int:
+    """Bytes of device workspace ring_ffn_bwd needs for these shapes."""
+    n = load().ring_ffn_bwd_workspace(int(rows), int(d_model), int(d_ff), int(chunk_rows))
+    _check(int(min(n, 0)))
+    return int(n)
+
+
+def ring_ffn_bwd(x, w1, w2, dout, dx, dw1, dw2, work, chunk_rows, stream=None):
+    """Backward of ring_ffn_fwd: dx [rows, d_model] bf16 is written, dw1
+    [d_ff, d_model] and dw2 [d_model, d_ff] fp32 are accumulated; work is a
+    uint8 device tensor of at least ring_ffn_bwd_workspace(...) bytes."""
+    for t, n in ((x, "x"), (w1, "w1"), (w2, "w2"), (dout, "dout"), (dx, "dx")):
+        _need(t, torch.bfloat16, n)
+    _need(dw1, torch.float32, "dw1")
+    _need(dw2, torch.float32, "dw2")
+    rows, d_model = x.shape
+    d_ff = w1.shape[0]
+    if tuple(w1.shape) != (d_ff, d_model) or tuple(w2.shape) != (d_model, d_ff):
+        raise ValueError("w1 must be [d_ff, d_model] and w2 [d_model, d_ff]")
+    if tuple(dout.shape) != (rows, d_model) or tuple(dx.shape) != (rows, d_model):
+        raise ValueError("dout and dx must be [rows, d_model]")
+    if tuple(dw1.shape) != (d_ff, d_model) or tuple(dw2.shape) != (d_model, d_ff):
+        raise ValueError("dw1 must be [d_ff, d_model] and dw2 [d_model, d_ff]")
+    nbytes = work.numel() * work.element_size()
+    _check(load().ring_ffn_bwd(_ptr(x), _ptr(w1), _ptr(w2), _ptr(dout), _ptr(dx), _ptr(dw1),
+                               _ptr(dw2), _ptr(work), nbytes, rows, d_model, d_ff,
+                               int(chunk_rows), _stream(stream)))
 
 
 def ring_attn_combine(o_a, lse_a, o_b, lse_b, stream=None):

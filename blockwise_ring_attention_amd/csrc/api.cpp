@@ -22,10 +22,12 @@ thread_local std::string g_last_error;
 
 // ---- kernel timing: event pairs around launches, kept until read ---------
 enum Kind {
-  kFwdBf16 = 0, kFwdFp32, kBwdDq, kBwdDkv, kDecode, kDecodeFold, kFfnUp, kFfnDown, kKinds
+  kFwdBf16 = 0, kFwdFp32, kBwdDq, kBwdDkv, kDecode, kDecodeFold, kFfnUp, kFfnDown,
+  kFfnBwdGemm, kFfnBwdAux, kKinds
 };
-const char* const kKindNames[kKinds] = {"fwd_bf16",   "fwd_fp32",    "bwd_dq", "bwd_dkv",
-                                        "fwd_decode", "decode_fold", "ffn_up", "ffn_down"};
+const char* const kKindNames[kKinds] = {"fwd_bf16",   "fwd_fp32",    "bwd_dq",       "bwd_dkv",
+                                        "fwd_decode", "decode_fold", "ffn_up",       "ffn_down",
+                                        "ffn_bwd_gemm", "ffn_bwd_aux"};
 
 struct TimingRec {
   int kind;
@@ -250,6 +252,47 @@ int ra_check_decode(const ra_shape& s) {
   return RA_OK;
 }
 
+// Feedforward shapes shared by the forward and backward entry points.
+int ra_check_ffn(int64_t rows, int d_model, int d_ff, int chunk_rows) {
+  if (rows < 0 || rows > 0x7fffffffLL)
+    return ra_fail(RA_ERR_INVALID, "rows %lld outside [0, 2^31)", (long long)rows);
+  if (d_model < 256 || d_ff < 256 || d_model % 256 != 0 || d_ff % 256 != 0)
+    return ra_fail(RA_ERR_UNSUPPORTED, "d_model %d and d_ff %d must be positive multiples of 256",
+                   d_model, d_ff);
+  if (chunk_rows < 1) return ra_fail(RA_ERR_INVALID, "chunk_rows %d must be >= 1", chunk_rows);
+  const int64_t chunk = std::min<int64_t>(chunk_rows, std::max<int64_t>(rows, 1));
+  if (((chunk + 255) / 256) * (int64_t)(std::max(d_model, d_ff) / 256) > 0x7fffffffLL)
+    return ra_fail(RA_ERR_INVALID, "problem too large for one launch");
+  return RA_OK;
+}
+
+// Backward workspace, in order (each part 256-byte aligned): W1^T [dm x dff],
+// W2^T [dff x dm], Z, H and G (the hidden gradient) [c x dff], and the
+// zero-padded transposes x^T, dout^T [dm x cp], G^T, H^T [dff x cp], with
+// c = min(rows, chunk_rows) and cp = c rounded up to a multiple of 64.
+struct FfnBwdWork {
+  size_t w1t, w2t, z, h, g, xt, dot, gt, ht, total;
+};
+FfnBwdWork ra_ffn_bwd_layout(int64_t rows, int d_model, int d_ff, int chunk_rows) {
+  const int64_t c = std::min<int64_t>(chunk_rows, std::max<int64_t>(rows, 1));
+  const int64_t cp = (c + 63) / 64 * 64;
+  const size_t dm = (size_t)d_model, df = (size_t)d_ff;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  FfnBwdWork w;
+  size_t off = 0;
+  w.w1t = off; off += up(dm * df * 2);
+  w.w2t = off; off += up(dm * df * 2);
+  w.z = off;   off += up((size_t)c * df * 2);
+  w.h = off;   off += up((size_t)c * df * 2);
+  w.g = off;   off += up((size_t)c * df * 2);
+  w.xt = off;  off += up(dm * (size_t)cp * 2);
+  w.dot = off; off += up(dm * (size_t)cp * 2);
+  w.gt = off;  off += up(df * (size_t)cp * 2);
+  w.ht = off;  off += up(df * (size_t)cp * 2);
+  w.total = off;
+  return w;
+}
+
 int ra_decode_splits(const ra_shape& s, int k_chunk) {
   return (int)(((int64_t)s.Lk + k_chunk - 1) / k_chunk);
 }
@@ -258,7 +301,7 @@ int ra_decode_splits(const ra_shape& s, int k_chunk) {
 
 extern "C" {
 
-int ring_attn_version(void) { return 202; }
+int ring_attn_version(void) { return 203; }
 
 int ring_attn_timing_enable(int on) {
   std::lock_guard<std::mutex> g(g_tmu);
@@ -459,17 +502,11 @@ int ring_attn_fwd_decode(const void* q, const void* kv_block, int k_chunk, float
 
 int ring_ffn_fwd(const void* x, const void* w1, const void* w2, void* hidden, void* out,
                  int64_t rows, int d_model, int d_ff, int chunk_rows, void* stream) {
-  if (rows < 0 || rows > 0x7fffffffLL)
-    return ra_fail(RA_ERR_INVALID, "rows %lld outside [0, 2^31)", (long long)rows);
-  if (d_model < 256 || d_ff < 256 || d_model % 256 != 0 || d_ff % 256 != 0)
-    return ra_fail(RA_ERR_UNSUPPORTED, "d_model %d and d_ff %d must be positive multiples of 256",
-                   d_model, d_ff);
-  if (chunk_rows < 1) return ra_fail(RA_ERR_INVALID, "chunk_rows %d must be >= 1", chunk_rows);
+  int rc = ra_check_ffn(rows, d_model, d_ff, chunk_rows);
+  if (rc) return rc;
   if (rows == 0) return RA_OK;
   if (!x || !w1 || !w2 || !hidden || !out) return ra_fail(RA_ERR_INVALID, "NULL tensor pointer");
   const int64_t chunk = std::min<int64_t>(chunk_rows, rows);
-  if (((chunk + 255) / 256) * (int64_t)(std::max(d_model, d_ff) / 256) > 0x7fffffffLL)
-    return ra_fail(RA_ERR_INVALID, "problem too large for one launch");
   const size_t xb = (size_t)rows * d_model * 2, w1b = (size_t)d_ff * d_model * 2,
                w2b = w1b, hb = (size_t)chunk * d_ff * 2, ob = xb;
   const void* ins[3] = {x, w1, w2};
@@ -491,6 +528,86 @@ int ring_ffn_fwd(const void* x, const void* w1, const void* w2, void* hidden, vo
                            st);
     td.done();
     if (e != hipSuccess) return ra_hip_fail(e, "feedforward down-projection launch");
+  }
+  return RA_OK;
+}
+
+int64_t ring_ffn_bwd_workspace(int64_t rows, int d_model, int d_ff, int chunk_rows) {
+  int rc = ra_check_ffn(rows, d_model, d_ff, chunk_rows);
+  if (rc) return rc;
+  return (int64_t)ra_ffn_bwd_layout(rows, d_model, d_ff, chunk_rows).total;
+}
+
+int ring_ffn_bwd(const void* x, const void* w1, const void* w2, const void* dout, void* dx,
+                 float* dw1, float* dw2, void* work, int64_t work_bytes, int64_t rows,
+                 int d_model, int d_ff, int chunk_rows, void* stream) {
+  int rc = ra_check_ffn(rows, d_model, d_ff, chunk_rows);
+  if (rc) return rc;
+  if (rows == 0) return RA_OK;
+  if (!x || !w1 || !w2 || !dout || !dx || !dw1 || !dw2 || !work)
+    return ra_fail(RA_ERR_INVALID, "NULL tensor pointer");
+  const FfnBwdWork L = ra_ffn_bwd_layout(rows, d_model, d_ff, chunk_rows);
+  if (work_bytes < (int64_t)L.total)
+    return ra_fail(RA_ERR_INVALID, "workspace of %lld bytes is smaller than the %lld needed",
+                   (long long)work_bytes, (long long)L.total);
+  const size_t xb = (size_t)rows * d_model * 2, wb = (size_t)d_ff * d_model * 2;
+  const void* ins[4] = {x, w1, w2, dout};
+  const size_t insz[4] = {xb, wb, wb, xb};
+  void* outs[4] = {dx, dw1, dw2, work};
+  const size_t outsz[4] = {xb, wb * 2, wb * 2, L.total};
+  for (int o = 0; o < 4; ++o) {
+    for (int i = 0; i < 4; ++i)
+      if (overlaps(outs[o], outsz[o], ins[i], insz[i]))
+        return ra_fail(RA_ERR_INVALID, "an output or the workspace overlaps an input");
+    for (int p = o + 1; p < 4; ++p)
+      if (overlaps(outs[o], outsz[o], outs[p], outsz[p]))
+        return ra_fail(RA_ERR_INVALID, "outputs or the workspace overlap each other");
+  }
+  hipStream_t st = (hipStream_t)stream;
+  char* wk = (char*)work;
+  void *w1t = wk + L.w1t, *w2t = wk + L.w2t, *z = wk + L.z, *h = wk + L.h, *g = wk + L.g;
+  void *xt = wk + L.xt, *dot = wk + L.dot, *gt = wk + L.gt, *ht = wk + L.ht;
+  auto fail = [](hipError_t e, const char* what) { return ra_hip_fail(e, what); };
+  hipError_t e;
+  {
+    Timed t(kFfnBwdAux, st);
+    e = ra_launch_transpose_pad(w1, w1t, d_ff, d_model, d_ff, st);  // W1^T [dm x dff]
+    if (e == hipSuccess) e = ra_launch_transpose_pad(w2, w2t, d_model, d_ff, d_model, st);
+    t.done();
+    if (e != hipSuccess) return fail(e, "weight transpose launch");
+  }
+  const int64_t chunk = std::min<int64_t>(chunk_rows, rows);
+  for (int64_t r0 = 0; r0 < rows; r0 += chunk) {
+    const int m = (int)std::min<int64_t>(chunk, rows - r0);
+    const int mp = (m + 63) / 64 * 64;
+    const char* xc = (const char*)x + (size_t)r0 * d_model * 2;
+    const char* dc = (const char*)dout + (size_t)r0 * d_model * 2;
+    char* dxc = (char*)dx + (size_t)r0 * d_model * 2;
+    {
+      Timed t(kFfnBwdGemm, st);
+      e = ra_launch_gemm_tn(xc, w1, z, m, d_ff, d_model, 0, st);          // Z = x W1^T
+      if (e == hipSuccess) e = ra_launch_gemm_tn(dc, w2t, g, m, d_ff, d_model, 0, st);  // G = dout W2
+      t.done();
+      if (e != hipSuccess) return fail(e, "feedforward backward product launch");
+    }
+    {
+      Timed t(kFfnBwdAux, st);
+      e = ra_launch_gelu_grad(z, g, h, (int64_t)m * d_ff, st);           // H, G <- G GELU'(Z)
+      if (e == hipSuccess) e = ra_launch_transpose_pad(xc, xt, m, d_model, mp, st);
+      if (e == hipSuccess) e = ra_launch_transpose_pad(dc, dot, m, d_model, mp, st);
+      if (e == hipSuccess) e = ra_launch_transpose_pad(g, gt, m, d_ff, mp, st);
+      if (e == hipSuccess) e = ra_launch_transpose_pad(h, ht, m, d_ff, mp, st);
+      t.done();
+      if (e != hipSuccess) return fail(e, "feedforward backward elementwise launch");
+    }
+    {
+      Timed t(kFfnBwdGemm, st);
+      e = ra_launch_gemm_tn(g, w1t, dxc, m, d_model, d_ff, 0, st);        // dx = G W1
+      if (e == hipSuccess) e = ra_launch_gemm_tn(gt, xt, dw1, d_ff, d_model, mp, 1, st);  // dW1 += G^T x
+      if (e == hipSuccess) e = ra_launch_gemm_tn(dot, ht, dw2, d_model, d_ff, mp, 1, st);  // dW2 += dout^T H
+      t.done();
+      if (e != hipSuccess) return fail(e, "feedforward backward product launch");
+    }
   }
   return RA_OK;
 }

@@ -129,20 +129,29 @@ __device__ __forceinline__ void wait_steps_pending(int pending) {
 // z < 0, so no 1 - erf cancellation is formed.  In fp32 with the hardware
 // exp2 and reciprocal, |GELU error| < 5e-7 (checked against the exact form),
 // well below the bf16 rounding of the hidden activation that follows.
-__device__ __forceinline__ float gelu(float z) {
+__device__ __forceinline__ float normal_cdf(float z) {
   constexpr float p = 0.3275911f, a1 = 0.254829592f, a2 = -0.284496736f, a3 = 1.421413741f,
                   a4 = -1.453152027f, a5 = 1.061405429f;
   const float u = fabsf(z) * 0.70710678118654752f;
   const float t = __builtin_amdgcn_rcpf(fmaf(p, u, 1.0f));
   const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, a5, a4), a3), a2), a1);
   const float ec = poly * exp2_fast(-u * u * kLog2e);
-  return z * (z >= 0.0f ? fmaf(-0.5f, ec, 1.0f) : 0.5f * ec);
+  return z >= 0.0f ? fmaf(-0.5f, ec, 1.0f) : 0.5f * ec;
+}
+__device__ __forceinline__ float gelu(float z) { return z * normal_cdf(z); }
+// d GELU / dz = Phi(z) + z phi(z), phi the standard normal density.
+__device__ __forceinline__ float gelu_grad(float z) {
+  const float dens = 0.3989422804014327f * exp2_fast(-0.5f * z * z * kLog2e);
+  return fmaf(z, dens, normal_cdf(z));
 }
 
 // C[m][n] = epi(sum_k A[m][k] B[n][k]) for m < M; N % 256 == 0, K % 64 == 0.
-template <bool GELU, int BK, int NSTAGE>
+// Epilogues: bf16 store, GELU then bf16 store, or fp32 accumulate (C += AB^T).
+enum { kEpiStore = 0, kEpiGelu = 1, kEpiAccF32 = 2 };
+
+template <int EPI, int BK, int NSTAGE>
 __global__ __launch_bounds__(256, 1) void gemm_tn_kernel(
-    const bf16* __restrict__ A, const bf16* __restrict__ B, bf16* __restrict__ C, int M,
+    const bf16* __restrict__ A, const bf16* __restrict__ B, void* __restrict__ Cv, int M,
     int N, int K, int tiles_m, int tiles_n) {
   using G = GemmCfg<BK, NSTAGE>;
   constexpr int ROWB = G::ROWB, DS = G::DS, PF = NSTAGE - 1;
@@ -254,49 +263,131 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_kernel(
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // Epilogue: each wave writes its quadrant (after the activation, as bf16)
-  // into the LDS tile, four adjacent columns per 8-byte write; then the
-  // workgroup stores the tile row by row, 16 bytes per lane.
   __syncthreads();  // every wave is done reading the last stage
+  if constexpr (EPI == kEpiAccF32) {
+    // fp32 accumulate, one 128-column half at a time: the waves owning that
+    // half stage it in LDS (16-byte writes, four adjacent columns), then the
+    // workgroup adds it to C row by row with 16-byte reads and writes.
+    float* Cf = (float*)Cv;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int half = 0; half < 2; ++half) {
+      if (wn == half) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 v;
+          for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float x = acc[i][j][4 * g + e];
-          if constexpr (GELU) x = gelu(x);
-          v[e] = (bf16)x;
-        }
-        const int row = wm * 128 + i * 32 + l32;
-        const int col = wn * 128 + j * 32 + 8 * g + 4 * hl;
-        *(bf16x4*)(smem + row * OUT_ROWB + col * 2) = v;
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                               acc[i][j][4 * g + 3]};
+              const int row = wm * 128 + i * 32 + l32;
+              const int col = j * 32 + 8 * g + 4 * hl;
+              *(f32x4*)(smem + row * OUT_ROWB + col * 4) = v;
+            }
       }
-  __syncthreads();
+      __syncthreads();
 #pragma unroll 4
-  for (int it = 0; it < BM * BN / 8 / 256; ++it) {
-    const int id = it * 256 + tid;
-    const int row = id >> 5, c = id & 31;   // 32 chunks of 8 columns per row
-    const u32x4 v = *(const u32x4*)(smem + row * OUT_ROWB + c * 16);
-    if (m0 + row < M) *(u32x4*)(C + (size_t)(m0 + row) * N + n0 + c * 8) = v;
+      for (int it = 0; it < BM * 128 / 4 / 256; ++it) {
+        const int id = it * 256 + tid;
+        const int row = id >> 5, c = id & 31;   // 32 chunks of 4 columns per row
+        const f32x4 v = *(const f32x4*)(smem + row * OUT_ROWB + c * 16);
+        if (m0 + row < M) {
+          f32x4* dst = (f32x4*)(Cf + (size_t)(m0 + row) * N + n0 + half * 128 + c * 4);
+          *dst = *dst + v;
+        }
+      }
+      __syncthreads();
+    }
+  } else {
+    // Each wave writes its quadrant (after the activation, as bf16) into
+    // the LDS tile, four adjacent columns per 8-byte write; then the
+    // workgroup stores the tile row by row, 16 bytes per lane.
+    bf16* C = (bf16*)Cv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float x = acc[i][j][4 * g + e];
+            if constexpr (EPI == kEpiGelu) x = gelu(x);
+            v[e] = (bf16)x;
+          }
+          const int row = wm * 128 + i * 32 + l32;
+          const int col = wn * 128 + j * 32 + 8 * g + 4 * hl;
+          *(bf16x4*)(smem + row * OUT_ROWB + col * 2) = v;
+        }
+    __syncthreads();
+#pragma unroll 4
+    for (int it = 0; it < BM * BN / 8 / 256; ++it) {
+      const int id = it * 256 + tid;
+      const int row = id >> 5, c = id & 31;   // 32 chunks of 8 columns per row
+      const u32x4 v = *(const u32x4*)(smem + row * OUT_ROWB + c * 16);
+      if (m0 + row < M) *(u32x4*)(C + (size_t)(m0 + row) * N + n0 + c * 8) = v;
+    }
   }
+}
+
+// out[c][r] = in[r][c] for r < R and 0 for R <= r < Rpad: a [R x C] bf16
+// matrix into a [C x Rpad] one (C and Rpad multiples of 64), one 64 x 64
+// tile per workgroup through LDS, 16-byte global reads and writes.
+__global__ __launch_bounds__(256) void transpose_pad_kernel(const bf16* __restrict__ in,
+                                                            bf16* __restrict__ out, int R, int C,
+                                                            int Rpad) {
+  constexpr int TROW = 64 + 8;   // padded LDS row (elements)
+  __shared__ bf16 tile[64 * TROW];
+  const int tiles_c = C / 64;
+  const int r0 = (blockIdx.x / tiles_c) * 64, c0 = (blockIdx.x % tiles_c) * 64;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int row = t / 8 + 32 * k, ch = t % 8;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r0 + row < R) v = *(const u32x4*)(in + (size_t)(r0 + row) * C + c0 + ch * 8);
+    *(u32x4*)(tile + row * TROW + ch * 8) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int orow = t / 8 + 32 * k, ch = t % 8;   // output row = input column
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = tile[(ch * 8 + e) * TROW + orow];
+    *(bf16x8*)(out + (size_t)(c0 + orow) * Rpad + r0 + ch * 8) = v;
+  }
+}
+
+// Per element: h = GELU(z), g <- g * GELU'(z) (the gradient with respect to
+// the pre-activation, in place of the gradient with respect to h).  n % 8 == 0.
+__global__ __launch_bounds__(256) void gelu_grad_kernel(const bf16* __restrict__ Z,
+                                                        bf16* __restrict__ G,
+                                                        bf16* __restrict__ H, int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const bf16x8 z = *(const bf16x8*)(Z + 8 * i);
+  const bf16x8 g = *(const bf16x8*)(G + 8 * i);
+  bf16x8 h, dz;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float zf = (float)z[e];
+    h[e] = (bf16)gelu(zf);
+    dz[e] = (bf16)((float)g[e] * gelu_grad(zf));
+  }
+  *(bf16x8*)(H + 8 * i) = h;
+  *(bf16x8*)(G + 8 * i) = dz;
 }
 
 constexpr int kBK = 64, kStages = 2;
 
-hipError_t gemm_tn(const bf16* A, const bf16* B, bf16* C, int M, int N, int K, bool gelu_epi,
+template <int EPI>
+hipError_t gemm_tn(const bf16* A, const bf16* B, void* C, int M, int N, int K,
                    hipStream_t stream) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
-  const dim3 grid((unsigned)(tiles_m * tiles_n)), block(256);
-  if (gelu_epi)
-    hipLaunchKernelGGL((gemm_tn_kernel<true, kBK, kStages>), grid, block, 0, stream, A, B, C, M,
-                       N, K, tiles_m, tiles_n);
-  else
-    hipLaunchKernelGGL((gemm_tn_kernel<false, kBK, kStages>), grid, block, 0, stream, A, B, C,
-                       M, N, K, tiles_m, tiles_n);
+  hipLaunchKernelGGL((gemm_tn_kernel<EPI, kBK, kStages>), dim3((unsigned)(tiles_m * tiles_n)),
+                     dim3(256), 0, stream, A, B, C, M, N, K, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -305,13 +396,40 @@ hipError_t gemm_tn(const bf16* A, const bf16* B, bf16* C, int M, int N, int K, b
 hipError_t ra_launch_ffn_up(const void* x, const void* w1, void* hidden, int rows, int d_model,
                             int d_ff, hipStream_t stream) {
   if (rows < 1 || d_model % 64 != 0 || d_ff % BN != 0) return hipErrorInvalidValue;
-  return gemm_tn((const bf16*)x, (const bf16*)w1, (bf16*)hidden, rows, d_ff, d_model, true,
-                 stream);
+  return gemm_tn<kEpiGelu>((const bf16*)x, (const bf16*)w1, hidden, rows, d_ff, d_model, stream);
 }
 
 hipError_t ra_launch_ffn_down(const void* hidden, const void* w2, void* out, int rows,
                               int d_model, int d_ff, hipStream_t stream) {
   if (rows < 1 || d_ff % 64 != 0 || d_model % BN != 0) return hipErrorInvalidValue;
-  return gemm_tn((const bf16*)hidden, (const bf16*)w2, (bf16*)out, rows, d_model, d_ff, false,
-                 stream);
+  return gemm_tn<kEpiStore>((const bf16*)hidden, (const bf16*)w2, out, rows, d_model, d_ff,
+                            stream);
+}
+
+hipError_t ra_launch_gemm_tn(const void* a, const void* b, void* c, int m, int n, int k,
+                             int accumulate_f32, hipStream_t stream) {
+  if (m < 1 || n % BN != 0 || k % 64 != 0 || k < 64) return hipErrorInvalidValue;
+  return accumulate_f32
+             ? gemm_tn<kEpiAccF32>((const bf16*)a, (const bf16*)b, c, m, n, k, stream)
+             : gemm_tn<kEpiStore>((const bf16*)a, (const bf16*)b, c, m, n, k, stream);
+}
+
+hipError_t ra_launch_transpose_pad(const void* in, void* out, int rows, int cols, int rows_pad,
+                                   hipStream_t stream) {
+  if (rows < 0 || cols % 64 != 0 || rows_pad % 64 != 0 || rows_pad < rows)
+    return hipErrorInvalidValue;
+  const long long tiles = (long long)(rows_pad / 64) * (cols / 64);
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_pad_kernel, dim3((unsigned)tiles), dim3(256), 0, stream,
+                     (const bf16*)in, (bf16*)out, rows, cols, rows_pad);
+  return hipGetLastError();
+}
+
+hipError_t ra_launch_gelu_grad(const void* z, void* g, void* h, int64_t n, hipStream_t stream) {
+  if (n % 8 != 0) return hipErrorInvalidValue;
+  const int64_t n8 = n / 8;
+  if (n8 == 0) return hipSuccess;
+  hipLaunchKernelGGL(gelu_grad_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
+                     (const bf16*)z, (bf16*)g, (bf16*)h, n8);
+  return hipGetLastError();
 }

@@ -81,5 +81,13 @@ def draw_ffn(cfg: FfnConfig, seed: int = 0):
     return tuple(out)
 
 
+def draw_ffn_dout(cfg: FfnConfig, seed: int = 0) -> torch.Tensor:
+    """Upstream gradient of the feedforward's output, [rows, d_model] ~ N(0, 1),
+    bf16 (RNE from float32)."""
+    a = _rng(seed, cfg.cfg_id, "do", 0).standard_normal((cfg.rows, cfg.d_model),
+                                                        dtype=np.float32)
+    return torch.from_numpy(a).to(torch.bfloat16)
+
+
 def torch_dtype(cfg: ShareConfig | DecodeConfig) -> torch.dtype:
     return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32

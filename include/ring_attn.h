@@ -210,6 +210,30 @@ int ring_ffn_fwd(const void* x, const void* w1, const void* w2, void* hidden,
                  void* out, int64_t rows, int d_model, int d_ff, int chunk_rows,
                  void* stream);
 
+/* Backward of ring_ffn_fwd for the same rows and chunking: given
+ * dout = d loss / d out [rows, d_model] bf16,
+ *   dx   = dZ W1                    [rows, d_model]  bf16 (written)
+ *   dw1 += dZ^T x                   [d_ff, d_model]  fp32 (accumulated)
+ *   dw2 += dout^T GELU(Z)           [d_model, d_ff]  fp32 (accumulated)
+ * with Z = x W1^T recomputed per chunk, dH = dout W2 and
+ * dZ = dH * GELU'(Z), GELU'(z) = Phi(z) + z phi(z) (the pages do not
+ * discuss the backward; this is the exact gradient of the forward above).
+ * Z, GELU(Z) and dZ are held in bf16; products accumulate in fp32, and dw1
+ * / dw2 gather every chunk's contribution, so callers zero them first (or
+ * keep accumulating over several blocks).  work is a caller-provided device
+ * workspace of ring_ffn_bwd_workspace(rows, d_model, d_ff, chunk_rows)
+ * bytes (transposed weights and per-chunk activations; contents on return
+ * are unspecified); a smaller work_bytes is RA_ERR_INVALID.  Outputs and
+ * the workspace must not overlap each other or any input.  Shape rules as
+ * for ring_ffn_fwd.  ring_ffn_bwd_workspace returns the byte count (>= 0) or
+ * a negative error code. */
+int64_t ring_ffn_bwd_workspace(int64_t rows, int d_model, int d_ff,
+                               int chunk_rows);
+int ring_ffn_bwd(const void* x, const void* w1, const void* w2,
+                 const void* dout, void* dx, float* dw1, float* dw2, void* work,
+                 int64_t work_bytes, int64_t rows, int d_model, int d_ff,
+                 int chunk_rows, void* stream);
+
 /* ---- single-GPU ring emulator ------------------------------------------
  * Plays one member of a ring of ring_size members on one GPU.  The other
  * members' key/value blocks live in a device pool; the "hop" that would
@@ -260,7 +284,9 @@ int ring_emu_bwd(const void* q, const void* const* kv_pool, void* slot0,
  * a pair of HIP events recorded on the stream the kernel runs on.  Kernel
  * families: "fwd_bf16", "fwd_fp32", "bwd_dq", "bwd_dkv", "fwd_decode" (the
  * split kernel of ring_attn_fwd_decode), "decode_fold" (its fold), and
- * "ffn_up" / "ffn_down" (the two products of ring_ffn_fwd, per chunk).
+ * "ffn_up" / "ffn_down" (the two products of ring_ffn_fwd, per chunk),
+ * "ffn_bwd_gemm" / "ffn_bwd_aux" (ring_ffn_bwd's products, and its
+ * transposes and activation-gradient passes, in groups).
  * ring_attn_timing_enable(on): on != 0 discards earlier records and starts
  * collecting; 0 stops collecting (records are kept).
  * ring_attn_timing_read(name, &launches, &total_ms): waits for the recorded

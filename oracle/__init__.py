@@ -19,6 +19,7 @@ What it computes
   that the blockwise feedforward computes chunk by chunk (Ring Attention
   with Blockwise Transformers, abstract: blockwise computation of
   self-attention and feedforward; the form is a reading, the pages give none).
+* ``ffn.feedforward_grads``: its closed-form gradient (dx, dW1, dW2).
 * ``brute``: scalar triple loops with ``math.exp`` / ``math.fsum`` for tiny
   shapes.
 * ``ring``: a separate fp64 emulation of the ring schedule, the chunked online
@@ -33,8 +34,9 @@ fp64 autograd and SDPA as independent library routines, gradient sum
 identities, combine associativity / commutativity / identity.
 """
 from .exact import attention, attention_grads, positions
-from .ffn import feedforward, gelu
+from .ffn import feedforward, feedforward_grad_magnitudes, feedforward_grads, gelu, gelu_grad
 from .ring import combine, block_partial, ring_share, ring_schedule
 
 __all__ = ["attention", "attention_grads", "positions", "combine",
-           "block_partial", "ring_share", "ring_schedule", "feedforward", "gelu"]
+           "block_partial", "ring_share", "ring_schedule", "feedforward", "feedforward_grads",
+           "feedforward_grad_magnitudes", "gelu", "gelu_grad"]

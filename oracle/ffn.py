@@ -11,7 +11,10 @@ transformer layer,
     FFN(x) = GELU(x W1^T) W2^T,     GELU(z) = z Phi(z) = z/2 (1 + erf(z/sqrt 2)),
 
 applied to every row of x independently, with W1 [d_ff, d_model] and W2
-[d_model, d_ff] in the (out, in) layout of a linear layer.  Because it is
+[d_model, d_ff] in the (out, in) layout of a linear layer.  The gradients
+(the pages do not discuss the backward) are those of sum(dOut * FFN(x)):
+with Z = x W1^T, H = GELU(Z), dH = dOut W2 and dZ = dH * GELU'(Z),
+GELU'(z) = Phi(z) + z phi(z):  dx = dZ W1,  dW1 = dZ^T x,  dW2 = dOut^T H.  Because it is
 position-wise, computing it a chunk of rows at a time (the blockwise form)
 gives the same rows; the oracle therefore evaluates all rows at once, with
 no rounding of the hidden activation.
@@ -41,3 +44,35 @@ def feedforward(x, w1, w2):
     if w1.shape[1] != x.shape[1] or w2.shape != (w1.shape[1], w1.shape[0]):
         raise ValueError(f"shapes x {x.shape}, w1 {w1.shape}, w2 {w2.shape} do not chain")
     return gelu(x @ w1.T) @ w2.T
+
+
+def gelu_grad(z):
+    """d GELU / dz = Phi(z) + z phi(z), phi the standard normal density."""
+    z = np.asarray(z, dtype=np.float64)
+    return 0.5 * (1.0 + erf(z / np.sqrt(2.0))) + z * np.exp(-0.5 * z * z) / np.sqrt(2.0 * np.pi)
+
+
+def feedforward_grads(x, w1, w2, dout):
+    """Gradients of sum(dout * FFN(x)) with respect to x, W1 and W2, float64:
+    returns (dx [rows, d_model], dw1 [d_ff, d_model], dw2 [d_model, d_ff])."""
+    x, w1, w2, dout = _as64(x), _as64(w1), _as64(w2), _as64(dout)
+    if w1.shape[1] != x.shape[1] or w2.shape != (w1.shape[1], w1.shape[0]):
+        raise ValueError(f"shapes x {x.shape}, w1 {w1.shape}, w2 {w2.shape} do not chain")
+    if dout.shape != x.shape:
+        raise ValueError(f"dout {dout.shape} does not match x {x.shape}")
+    z = x @ w1.T
+    h = gelu(z)
+    dz = (dout @ w2) * gelu_grad(z)
+    return dz @ w1, dz.T @ x, dout.T @ h
+
+
+def feedforward_grad_magnitudes(x, w1, w2, dout):
+    """Sums of the absolute values of the terms behind each gradient entry:
+    (|dZ| |W1|, |dZ|^T |x|, |dOut|^T |H|), float64, same shapes as
+    feedforward_grads.  An entry whose terms cancel has a small value but a
+    large sum of magnitudes; rounding each term by a relative e moves the
+    entry by at most e times this sum."""
+    x, w1, w2, dout = _as64(x), _as64(w1), _as64(w2), _as64(dout)
+    z = x @ w1.T
+    dz = np.abs((dout @ w2) * gelu_grad(z))
+    return dz @ np.abs(w1), dz.T @ np.abs(x), np.abs(dout).T @ np.abs(gelu(z))

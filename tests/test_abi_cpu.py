@@ -31,7 +31,8 @@ def test_header_declares_the_boundary():
     for n in ("ring_attn_fwd", "ring_attn_combine", "ring_attn_bwd", "ring_attn_bwd_prep",
               "ring_attn_finalize", "ring_attn_init_acc", "ring_attn_last_error",
               "ring_attn_version", "ring_emu_fwd", "ring_emu_bwd", "ring_attn_fwd_decode",
-              "ring_attn_decode_chunk", "ring_attn_decode_splits", "ring_ffn_fwd"):
+              "ring_attn_decode_chunk", "ring_attn_decode_splits", "ring_ffn_fwd",
+              "ring_ffn_bwd", "ring_ffn_bwd_workspace"):
         assert n in names
     assert sorted(_lib.EXPORTS) == names, "binding and header disagree"
 
@@ -39,7 +40,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.ring_attn_version() == 202
+    assert lib.ring_attn_version() == 203
     assert lib.ring_attn_last_error() == b""
 
 
@@ -198,6 +199,44 @@ def test_ffn_rejects_invalid_and_unsupported(lib):
 
 def test_ffn_empty_is_a_no_op(lib):
     assert _ffn(lib, rows=0, x=None, w1=None, w2=None, hidden=None, out=None) == 0
+
+
+def test_ffn_bwd_workspace_size(lib):
+    ws = lib.ring_ffn_bwd_workspace
+    # W1^T, W2^T; Z, H, G [c x dff]; x^T, dout^T [dm x cp]; G^T, H^T [dff x cp]
+    dm, dff, c = 256, 512, 300
+    cp = 320
+    want = 2 * (dm * dff * 2) + 3 * (c * dff * 2) + 2 * (dm * cp * 2) + 2 * (dff * cp * 2)
+    assert ws(300, dm, dff, 4096) == want          # chunk larger than rows: c = rows
+    assert ws(1000, dm, dff, 300) == want
+    assert ws(0, dm, dff, 64) > 0
+    assert ws(10, 200, dff, 64) == -2
+    assert ws(10, dm, dff, 0) == -1
+
+
+def _ffn_bwd(lib, rows=300, dm=256, dff=512, chunk=128, work_bytes=1 << 30, **ptrs):
+    p = dict(x=FAKE, w1=ctypes.c_void_p(0x1000000), w2=ctypes.c_void_p(0x2000000),
+             dout=ctypes.c_void_p(0x3000000), dx=ctypes.c_void_p(0x4000000),
+             dw1=ctypes.c_void_p(0x5000000), dw2=ctypes.c_void_p(0x6000000),
+             work=ctypes.c_void_p(0x10000000))
+    p.update(ptrs)
+    return lib.ring_ffn_bwd(p["x"], p["w1"], p["w2"], p["dout"], p["dx"], p["dw1"], p["dw2"],
+                            p["work"], work_bytes, rows, dm, dff, chunk, None)
+
+
+def test_ffn_bwd_rejects_invalid(lib):
+    assert _ffn_bwd(lib, dm=128) == -2
+    assert _ffn_bwd(lib, chunk=0) == -1
+    assert _ffn_bwd(lib, rows=-3) == -1
+    for name in ("x", "w1", "w2", "dout", "dx", "dw1", "dw2", "work"):
+        assert _ffn_bwd(lib, **{name: None}) == -1, name
+    assert _ffn_bwd(lib, work_bytes=1000) == -1                          # workspace too small
+    assert b"workspace" in lib.ring_attn_last_error()
+    assert _ffn_bwd(lib, dx=ctypes.c_void_p(0x1000 + 512)) == -1         # dx overlaps x
+    assert _ffn_bwd(lib, dw2=ctypes.c_void_p(0x5000000 + 4096)) == -1    # dw2 overlaps dw1
+    assert _ffn_bwd(lib, work=ctypes.c_void_p(0x3000000 + 64)) == -1     # work overlaps dout
+    none = {k: None for k in ("x", "w1", "w2", "dout", "dx", "dw1", "dw2", "work")}
+    assert _ffn_bwd(lib, rows=0, work_bytes=0, **none) == 0              # nothing to do
 
 
 def test_emulator_rejects_bad_schedules(lib):

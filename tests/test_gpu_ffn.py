@@ -11,8 +11,8 @@ import torch
 import oracle
 from blockwise_ring_attention_amd import _lib
 from blockwise_ring_attention_amd.configs import FFN_CONFIGS, FfnConfig
-from blockwise_ring_attention_amd.inputs import draw_ffn
-from tests._gates import check
+from blockwise_ring_attention_amd.inputs import draw_ffn, draw_ffn_dout
+from tests._gates import check, check_sum
 
 pytestmark = pytest.mark.gpu
 
@@ -70,3 +70,83 @@ def test_ffn_full_size_sampled_rows():
     rows = np.array(sorted(rows))
     ref = oracle.feedforward(x[rows], w1, w2)
     check("out", out[rows], ref, "bf16")
+
+
+# ---- backward ----------------------------------------------------------------
+
+def _run_bwd(x, w1, w2, dout, chunk, dw1=None, dw2=None):
+    dev = torch.device("cuda:0")
+    rows, d_model = x.shape
+    d_ff = w1.shape[0]
+    xd, w1d, w2d, dd = (t.to(dev) for t in (x, w1, w2, dout))
+    dx = torch.empty((rows, d_model), dtype=torch.bfloat16, device=dev)
+    dw1 = torch.zeros((d_ff, d_model), dtype=torch.float32, device=dev) if dw1 is None else dw1
+    dw2 = torch.zeros((d_model, d_ff), dtype=torch.float32, device=dev) if dw2 is None else dw2
+    nbytes = _lib.ring_ffn_bwd_workspace(rows, d_model, d_ff, chunk)
+    work = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _lib.ring_ffn_bwd(xd, w1d, w2d, dd, dx, dw1, dw2, work, chunk)
+    torch.cuda.synchronize()
+    return dx.cpu(), dw1, dw2
+
+
+BWD = [
+    # (name, rows, d_model, d_ff, chunk_rows)
+    ("one row", 1, 256, 256, 64),
+    ("ragged rows, chunks off the tile grid", 300, 256, 512, 100),
+    ("several tiles", 777, 512, 768, 512),
+]
+
+
+@pytest.mark.parametrize("case", BWD, ids=[c[0] for c in BWD])
+def test_ffn_backward_small_elementwise(case):
+    name, rows, dm, dff, chunk = case
+    print(name, flush=True)
+    cfg = FfnConfig(99, name, rows, dm, dff, chunk)
+    x, w1, w2 = draw_ffn(cfg, seed=5)
+    dout = draw_ffn_dout(cfg, seed=5)
+    dx, dw1, dw2 = _run_bwd(x, w1, w2, dout, chunk)
+    rdx, rdw1, rdw2 = oracle.feedforward_grads(x, w1, w2, dout)
+    mdx, mdw1, mdw2 = oracle.feedforward_grad_magnitudes(x, w1, w2, dout)
+    check_sum("dx", dx, rdx, mdx)
+    check_sum("dw1", dw1, rdw1, mdw1)
+    check_sum("dw2", dw2, rdw2, mdw2)
+
+
+def test_ffn_backward_accumulates_weight_gradients():
+    """dw1 / dw2 gather contributions: two calls give twice the gradient, and
+    dx does not depend on the chunking (bitwise)."""
+    cfg = FfnConfig(99, "acc", 600, 256, 512, 0)
+    x, w1, w2 = draw_ffn(cfg, seed=6)
+    dout = draw_ffn_dout(cfg, seed=6)
+    dx1, dw1, dw2 = _run_bwd(x, w1, w2, dout, 600)
+    one1, one2 = dw1.clone(), dw2.clone()
+    dx2, dw1, dw2 = _run_bwd(x, w1, w2, dout, 600, dw1, dw2)
+    torch.testing.assert_close(dw1, 2 * one1, rtol=1e-6, atol=1e-6)
+    torch.testing.assert_close(dw2, 2 * one2, rtol=1e-6, atol=1e-6)
+    assert torch.equal(dx1, dx2)
+    dx3, _, _ = _run_bwd(x, w1, w2, dout, 128)
+    assert torch.equal(dx1, dx3)
+
+
+def test_ffn_backward_full_size_sampled():
+    """The benchmark's workload: dx on sampled rows; dW1 rows and dW2 columns
+    of sampled hidden units (each hidden unit's weight gradients depend on
+    that unit alone, so the oracle computes them on the reduced layer)."""
+    cfg = FFN_CONFIGS["ffn-lwm7b"]
+    print(cfg.name + " backward", flush=True)
+    x, w1, w2 = draw_ffn(cfg, seed=0)
+    dout = draw_ffn_dout(cfg, seed=0)
+    dx, dw1, dw2 = _run_bwd(x, w1, w2, dout, cfg.chunk_rows)
+    rng = np.random.default_rng(1)
+    rows = np.array(sorted({0, 255, 256, cfg.chunk_rows - 1, cfg.chunk_rows, cfg.rows - 1}
+                           | set(rng.choice(cfg.rows, size=12, replace=False).tolist())))
+    rdx, _, _ = oracle.feedforward_grads(x[rows], w1, w2, dout[rows])
+    mdx, _, _ = oracle.feedforward_grad_magnitudes(x[rows], w1, w2, dout[rows])
+    check_sum("dx", dx[rows], rdx, mdx)
+    fs = np.array(sorted({0, 255, 256, cfg.d_ff - 1} |
+                         set(rng.choice(cfg.d_ff, size=8, replace=False).tolist())))
+    _, r1, r2 = oracle.feedforward_grads(x, w1[fs], w2[:, fs], dout)
+    _, m1, m2 = oracle.feedforward_grad_magnitudes(x, w1[fs], w2[:, fs], dout)
+    sel = torch.from_numpy(fs).cuda()
+    check_sum("dw1", dw1[sel].cpu(), r1, m1)
+    check_sum("dw2", dw2[:, sel].cpu(), r2, m2)

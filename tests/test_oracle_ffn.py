@@ -140,3 +140,123 @@ def test_planted_untransposed_weight_is_caught(which):
         return of.gelu(a) @ (w2 if which == "w2" else w2.T)
     assert _pin_torch(d_model=16, d_ff=16)
     assert not _pin_torch(slipped, d_model=16, d_ff=16)
+
+
+# ---- gradients -------------------------------------------------------------
+
+from oracle import feedforward_grads, gelu_grad  # noqa: E402
+
+
+def _pin_grad_table(gg=None):
+    """GELU'(z) = Phi(z) + z phi(z) at the printed table points and at -z."""
+    gg = gg or gelu_grad
+    g = json.load(open(os.path.join(GOLDEN, "ffn_gelu_table.json")))
+    ok = True
+    for k, phi in g["phi"].items():
+        z, dens = float(k), g["pdf"][k]
+        ok &= abs(float(gg(z)) - (phi + z * dens)) <= 1e-14
+        ok &= abs(float(gg(-z)) - ((1.0 - phi) - z * dens)) <= 1e-14
+    return ok
+
+
+def _pin_grads_autograd(grads=None, d_model=12, d_ff=20):
+    grads = grads or feedforward_grads
+    rng = np.random.default_rng(11)
+    x, w1, w2 = _rand(rng, 17, d_model, d_ff)
+    dout = rng.standard_normal((17, d_model))
+    t = [torch.from_numpy(a).requires_grad_(True) for a in (x, w1, w2)]
+    out = torch.nn.functional.linear(
+        torch.nn.functional.gelu(torch.nn.functional.linear(t[0], t[1]), approximate="none"), t[2])
+    (out * torch.from_numpy(dout)).sum().backward()
+    got = grads(x, w1, w2, dout)
+    return all(np.abs(g - r.grad.numpy()).max() <= 1e-12 for g, r in zip(got, t))
+
+
+def test_gelu_grad_matches_the_normal_table():
+    assert _pin_grad_table()
+
+
+def test_grads_torch_autograd_fp64():
+    assert _pin_grads_autograd()
+
+
+def test_grads_central_differences():
+    rng = np.random.default_rng(12)
+    x, w1, w2 = _rand(rng, 4, 3, 5)
+    dout = rng.standard_normal((4, 3))
+    dx, dw1, dw2 = feedforward_grads(x, w1, w2, dout)
+    eps = 1e-6
+
+    def loss(a, b, c):
+        return float((dout * feedforward(a, b, c)).sum())
+    for arr, grad, which in ((x, dx, 0), (w1, dw1, 1), (w2, dw2, 2)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            args = [x.copy(), w1.copy(), w2.copy()]
+            args[which][idx] += eps
+            up = loss(*args)
+            args[which][idx] -= 2 * eps
+            num[idx] = (up - loss(*args)) / (2 * eps)
+        np.testing.assert_allclose(grad, num, atol=1e-7, rtol=0)
+
+
+def test_hidden_units_are_independent():
+    """dW1 rows and dW2 columns of a set of hidden units come from those
+    units alone (the full-size GPU test samples them this way)."""
+    rng = np.random.default_rng(13)
+    x, w1, w2 = _rand(rng, 30, 8, 40)
+    dout = rng.standard_normal((30, 8))
+    _, dw1, dw2 = feedforward_grads(x, w1, w2, dout)
+    fs = np.array([0, 7, 39])
+    _, s1, s2 = feedforward_grads(x, w1[fs], w2[:, fs], dout)
+    np.testing.assert_allclose(s1, dw1[fs], atol=1e-13, rtol=0)
+    np.testing.assert_allclose(s2, dw2[:, fs], atol=1e-13, rtol=0)
+
+
+def _grad_missing_density(z):
+    z = np.asarray(z, dtype=np.float64)
+    return 0.5 * (1.0 + of.erf(z / np.sqrt(2.0)))
+
+
+def _grad_sign_slip(z):
+    z = np.asarray(z, dtype=np.float64)
+    return 0.5 * (1.0 + of.erf(z / np.sqrt(2.0))) - z * np.exp(-0.5 * z * z) / np.sqrt(2 * np.pi)
+
+
+@pytest.mark.parametrize("slip", [_grad_missing_density, _grad_sign_slip],
+                         ids=["no-density-term", "density-sign"])
+def test_planted_gelu_grad_slip_is_caught(monkeypatch, slip):
+    assert _pin_grad_table() and _pin_grads_autograd()
+    monkeypatch.setattr(of, "gelu_grad", slip)
+    assert not _pin_grad_table(of.gelu_grad)
+    assert not _pin_grads_autograd()
+
+
+def test_planted_weight_gradient_transposed_is_caught():
+    def slipped(x, w1, w2, dout):
+        dx, dw1, dw2 = feedforward_grads(x, w1, w2, dout)
+        return dx, dw1, dw2.T.reshape(dw2.shape)   # dW2 laid out as [d_ff, d_model]
+    assert not _pin_grads_autograd(slipped, d_model=12, d_ff=12)
+
+
+def test_grad_magnitudes_bound_each_gradient():
+    """The magnitude sums are, entry by entry, the sums of |terms| (checked by
+    brute force), and therefore bound the gradients themselves."""
+    from oracle import feedforward_grad_magnitudes
+    rng = np.random.default_rng(14)
+    x, w1, w2 = _rand(rng, 6, 4, 5)
+    dout = rng.standard_normal((6, 4))
+    dx, dw1, dw2 = feedforward_grads(x, w1, w2, dout)
+    mdx, mdw1, mdw2 = feedforward_grad_magnitudes(x, w1, w2, dout)
+    z = x @ w1.T
+    dz = (dout @ w2) * gelu_grad(z)
+    h = gelu(z)
+    for r in range(6):
+        for c in range(4):
+            assert abs(mdx[r, c] - math.fsum(abs(dz[r, f] * w1[f, c]) for f in range(5))) < 1e-12
+    for f in range(5):
+        for c in range(4):
+            assert abs(mdw1[f, c] - math.fsum(abs(dz[r, f] * x[r, c]) for r in range(6))) < 1e-12
+            assert abs(mdw2[c, f] - math.fsum(abs(dout[r, c] * h[r, f]) for r in range(6))) < 1e-12
+    for g, m in ((dx, mdx), (dw1, mdw1), (dw2, mdw2)):
+        assert (np.abs(g) <= m + 1e-12).all()
