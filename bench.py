@@ -132,6 +132,7 @@ KERNEL_SOURCES = {
     "fwd_decode": ["blockwise_ring_attention_amd/csrc/decode_bf16.hip"],
     "ffn_up": ["blockwise_ring_attention_amd/csrc/ffn_bf16.hip"],
     "ffn_down": ["blockwise_ring_attention_amd/csrc/ffn_bf16.hip"],
+    "ffn_bwd_gemm": ["blockwise_ring_attention_amd/csrc/ffn_bf16.hip"],
 }
 COMMON_SOURCE = "blockwise_ring_attention_amd/csrc/ra_common.h"
 
@@ -494,9 +495,8 @@ def _bench_ffn(args):
     dom = max(flops_fams, key=lambda f: per_kernel[f]["total_ms_per_step"])
     roofline = {"bound": "mfma", "achieved": per_kernel[dom]["tflops"], "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": per_kernel[dom]["frac"],
-                "traffic": (_measured_traffic(dom, FFN_TRAFFIC_FILE)
-                            if dom in ("ffn_up", "ffn_down") else None),
-                "traffic_unit": "HBM bytes per launch", "kernel": dom}
+                "traffic": _measured_traffic(dom, FFN_TRAFFIC_FILE),
+                "traffic_unit": "HBM bytes per product launch", "kernel": dom}
     result = {
         "metric": ("blockwise feedforward training-step TFLOP/s (fwd 4 + bwd 10 "
                    "·rows·d_model·d_ff); % of bf16 MFMA peak"),
