@@ -267,11 +267,11 @@ int ra_check_ffn(int64_t rows, int d_model, int d_ff, int chunk_rows) {
 }
 
 // Backward workspace, in order (each part 256-byte aligned): W1^T [dm x dff],
-// W2^T [dff x dm], Z, H and G (the hidden gradient) [c x dff], and the
+// W2^T [dff x dm], Z and G (the hidden gradient) [c x dff], and the
 // zero-padded transposes x^T, dout^T [dm x cp], G^T, H^T [dff x cp], with
 // c = min(rows, chunk_rows) and cp = c rounded up to a multiple of 64.
 struct FfnBwdWork {
-  size_t w1t, w2t, z, h, g, xt, dot, gt, ht, total;
+  size_t w1t, w2t, z, g, xt, dot, gt, ht, total;
 };
 FfnBwdWork ra_ffn_bwd_layout(int64_t rows, int d_model, int d_ff, int chunk_rows) {
   const int64_t c = std::min<int64_t>(chunk_rows, std::max<int64_t>(rows, 1));
@@ -283,7 +283,6 @@ FfnBwdWork ra_ffn_bwd_layout(int64_t rows, int d_model, int d_ff, int chunk_rows
   w.w1t = off; off += up(dm * df * 2);
   w.w2t = off; off += up(dm * df * 2);
   w.z = off;   off += up((size_t)c * df * 2);
-  w.h = off;   off += up((size_t)c * df * 2);
   w.g = off;   off += up((size_t)c * df * 2);
   w.xt = off;  off += up(dm * (size_t)cp * 2);
   w.dot = off; off += up(dm * (size_t)cp * 2);
@@ -565,7 +564,7 @@ int ring_ffn_bwd(const void* x, const void* w1, const void* w2, const void* dout
   }
   hipStream_t st = (hipStream_t)stream;
   char* wk = (char*)work;
-  void *w1t = wk + L.w1t, *w2t = wk + L.w2t, *z = wk + L.z, *h = wk + L.h, *g = wk + L.g;
+  void *w1t = wk + L.w1t, *w2t = wk + L.w2t, *z = wk + L.z, *g = wk + L.g;
   void *xt = wk + L.xt, *dot = wk + L.dot, *gt = wk + L.gt, *ht = wk + L.ht;
   auto fail = [](hipError_t e, const char* what) { return ra_hip_fail(e, what); };
   hipError_t e;
@@ -592,11 +591,10 @@ int ring_ffn_bwd(const void* x, const void* w1, const void* w2, const void* dout
     }
     {
       Timed t(kFfnBwdAux, st);
-      e = ra_launch_gelu_grad(z, g, h, (int64_t)m * d_ff, st);           // H, G <- G GELU'(Z)
+      // G <- G GELU'(Z) in place; G^T and GELU(Z)^T for the weight gradients
+      e = ra_launch_gelu_grad_transpose(z, g, gt, ht, m, d_ff, mp, st);
       if (e == hipSuccess) e = ra_launch_transpose_pad(xc, xt, m, d_model, mp, st);
       if (e == hipSuccess) e = ra_launch_transpose_pad(dc, dot, m, d_model, mp, st);
-      if (e == hipSuccess) e = ra_launch_transpose_pad(g, gt, m, d_ff, mp, st);
-      if (e == hipSuccess) e = ra_launch_transpose_pad(h, ht, m, d_ff, mp, st);
       t.done();
       if (e != hipSuccess) return fail(e, "feedforward backward elementwise launch");
     }

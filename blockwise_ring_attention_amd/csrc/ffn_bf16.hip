@@ -360,24 +360,53 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const bf16* __restri
   }
 }
 
-// Per element: h = GELU(z), g <- g * GELU'(z) (the gradient with respect to
-// the pre-activation, in place of the gradient with respect to h).  n % 8 == 0.
-__global__ __launch_bounds__(256) void gelu_grad_kernel(const bf16* __restrict__ Z,
-                                                        bf16* __restrict__ G,
-                                                        bf16* __restrict__ H, int64_t n8) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n8) return;
-  const bf16x8 z = *(const bf16x8*)(Z + 8 * i);
-  const bf16x8 g = *(const bf16x8*)(G + 8 * i);
-  bf16x8 h, dz;
+// The activation gradient and both transposes the weight gradients need, in
+// one pass over a 64 x 64 tile of the [R x C] chunk: per element
+// h = GELU(z) and g <- g * GELU'(z) (the gradient with respect to the
+// pre-activation, written back in place, row-major, for the dx product),
+// and the tile's g and h written transposed into Gt and Ht [C x Rpad], rows
+// R .. Rpad-1 of those zero.  C and Rpad multiples of 64.
+__global__ __launch_bounds__(256) void gelu_grad_transpose_kernel(
+    const bf16* __restrict__ Z, bf16* __restrict__ G, bf16* __restrict__ Gt,
+    bf16* __restrict__ Ht, int R, int C, int Rpad) {
+  constexpr int TROW = 64 + 8;   // padded LDS row (elements)
+  __shared__ bf16 tg[64 * TROW], th[64 * TROW];
+  const int tiles_c = C / 64;
+  const int r0 = (blockIdx.x / tiles_c) * 64, c0 = (blockIdx.x % tiles_c) * 64;
+  const int t = threadIdx.x;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float zf = (float)z[e];
-    h[e] = (bf16)gelu(zf);
-    dz[e] = (bf16)((float)g[e] * gelu_grad(zf));
+  for (int k = 0; k < 2; ++k) {
+    const int row = t / 8 + 32 * k, ch = t % 8;
+    bf16x8 dz = {}, h = {};
+    if (r0 + row < R) {
+      const size_t at = (size_t)(r0 + row) * C + c0 + ch * 8;
+      const bf16x8 z = *(const bf16x8*)(Z + at);
+      const bf16x8 g = *(const bf16x8*)(G + at);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float zf = (float)z[e];
+        h[e] = (bf16)gelu(zf);
+        dz[e] = (bf16)((float)g[e] * gelu_grad(zf));
+      }
+      *(bf16x8*)(G + at) = dz;
+    }
+    *(bf16x8*)(tg + row * TROW + ch * 8) = dz;
+    *(bf16x8*)(th + row * TROW + ch * 8) = h;
   }
-  *(bf16x8*)(H + 8 * i) = h;
-  *(bf16x8*)(G + 8 * i) = dz;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int orow = t / 8 + 32 * k, ch = t % 8;   // output row = input column
+    bf16x8 vg, vh;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      vg[e] = tg[(ch * 8 + e) * TROW + orow];
+      vh[e] = th[(ch * 8 + e) * TROW + orow];
+    }
+    const size_t at = (size_t)(c0 + orow) * Rpad + r0 + ch * 8;
+    *(bf16x8*)(Gt + at) = vg;
+    *(bf16x8*)(Ht + at) = vh;
+  }
 }
 
 constexpr int kBK = 64, kStages = 2;
@@ -425,11 +454,13 @@ hipError_t ra_launch_transpose_pad(const void* in, void* out, int rows, int cols
   return hipGetLastError();
 }
 
-hipError_t ra_launch_gelu_grad(const void* z, void* g, void* h, int64_t n, hipStream_t stream) {
-  if (n % 8 != 0) return hipErrorInvalidValue;
-  const int64_t n8 = n / 8;
-  if (n8 == 0) return hipSuccess;
-  hipLaunchKernelGGL(gelu_grad_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
-                     (const bf16*)z, (bf16*)g, (bf16*)h, n8);
+hipError_t ra_launch_gelu_grad_transpose(const void* z, void* g, void* gt, void* ht, int rows,
+                                         int cols, int rows_pad, hipStream_t stream) {
+  if (rows < 0 || cols % 64 != 0 || rows_pad % 64 != 0 || rows_pad < rows)
+    return hipErrorInvalidValue;
+  const long long tiles = (long long)(rows_pad / 64) * (cols / 64);
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(gelu_grad_transpose_kernel, dim3((unsigned)tiles), dim3(256), 0, stream,
+                     (const bf16*)z, (bf16*)g, (bf16*)gt, (bf16*)ht, rows, cols, rows_pad);
   return hipGetLastError();
 }

@@ -40,12 +40,15 @@ hipError_t ra_launch_ffn_down(const void* hidden, const void* w2, void* out, int
 //                  n % 256 == 0, k % 64 == 0, m >= 1
 //   transpose_pad: out [cols x rows_pad] = in [rows x cols] transposed, rows
 //                  rows .. rows_pad-1 of the result zero; cols, rows_pad % 64 == 0
-//   gelu_grad:     h = GELU(z), g <- g * GELU'(z) elementwise, n % 8 == 0
+//   gelu_grad_transpose: per element h = GELU(z), g <- g * GELU'(z) (in
+//                  place, [rows x cols]), and g, h written transposed into
+//                  gt, ht [cols x rows_pad] (rows .. rows_pad-1 zero)
 hipError_t ra_launch_gemm_tn(const void* a, const void* b, void* c, int m, int n, int k,
                              int accumulate_f32, hipStream_t stream);
 hipError_t ra_launch_transpose_pad(const void* in, void* out, int rows, int cols, int rows_pad,
                                    hipStream_t stream);
-hipError_t ra_launch_gelu_grad(const void* z, void* g, void* h, int64_t n, hipStream_t stream);
+hipError_t ra_launch_gelu_grad_transpose(const void* z, void* g, void* gt, void* ht, int rows,
+                                         int cols, int rows_pad, hipStream_t stream);
 hipError_t ra_launch_fwd_fp32(const float* q, const float* kv, float* o_acc,
                               float* lse_acc, const ra_launch& a);
 hipError_t ra_launch_init_acc(float* o_acc, float* lse_acc, int64_t rows,

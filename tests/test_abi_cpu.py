@@ -203,10 +203,10 @@ def test_ffn_empty_is_a_no_op(lib):
 
 def test_ffn_bwd_workspace_size(lib):
     ws = lib.ring_ffn_bwd_workspace
-    # W1^T, W2^T; Z, H, G [c x dff]; x^T, dout^T [dm x cp]; G^T, H^T [dff x cp]
+    # W1^T, W2^T; Z, G [c x dff]; x^T, dout^T [dm x cp]; G^T, H^T [dff x cp]
     dm, dff, c = 256, 512, 300
     cp = 320
-    want = 2 * (dm * dff * 2) + 3 * (c * dff * 2) + 2 * (dm * cp * 2) + 2 * (dff * cp * 2)
+    want = 2 * (dm * dff * 2) + 2 * (c * dff * 2) + 2 * (dm * cp * 2) + 2 * (dff * cp * 2)
     assert ws(300, dm, dff, 4096) == want          # chunk larger than rows: c = rows
     assert ws(1000, dm, dff, 300) == want
     assert ws(0, dm, dff, 64) > 0
