@@ -240,8 +240,8 @@ int ring_ffn_bwd(const void* x, const void* w1, const void* w2,
  * bring the next block over the interconnect is a device-to-device
  * hipMemcpyAsync into one of two receive slots, issued on side_stream and
  * overlapped with the attention of the current block on main_stream
- * (Ring Attention with Blockwise Transformers, abstract: communication of
- * key/value blocks overlapped with blockwise computation).  Events order
+ * (Ring Attention with Blockwise Transformers, abstract: the key/value
+ * transfers hide behind the blockwise compute).  Events order
  * copy-after-consume and compute-after-copy.  Only two slots exist: there
  * is never a gather of all blocks.
  *

@@ -11,14 +11,14 @@ What it computes
 * ``attention``: the plain definition of softmax attention with a causal mask
   over global token positions, O = softmax(scale * Q K^T + M) V, plus the
   natural-log log-sum-exp of every query row.  Ring attention is exact (Ring
-  Attention keyword page, definition: "without relying on approximations";
+  Attention keyword page, definition: no approximation is involved;
   Ring Attention with Blockwise Transformers, abstract), so the share of a
   ring member equals this definition restricted to the member's rows.
 * ``attention_grads``: the closed-form exact gradient of sum(dO * O).
 * ``ffn.feedforward``: the position-wise two-layer MLP GELU(x W1^T) W2^T
   that the blockwise feedforward computes chunk by chunk (Ring Attention
-  with Blockwise Transformers, abstract: blockwise computation of
-  self-attention and feedforward; the form is a reading, the pages give none).
+  with Blockwise Transformers, abstract: attention and the feedforward are
+  both computed block by block; the form is a reading, the pages give none).
 * ``ffn.feedforward_grads``: its closed-form gradient (dx, dW1, dW2).
 * ``brute``: scalar triple loops with ``math.exp`` / ``math.fsum`` for tiny
   shapes.

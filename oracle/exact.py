@@ -5,8 +5,9 @@ Test infrastructure only (see the package docstring).
 Ring Attention keyword page (definition) and the Ring Attention with
 Blockwise Transformers abstract state that the ring computes ordinary
 self-attention exactly, with no approximation; the darcstar commentary adds
-that the causal mask and the softmax denominator must be exact across chunk
-seams.  The oracle therefore writes out the definition directly:
+that the causal masking and the softmax normaliser have to stay exact
+across chunk seams.  The oracle therefore writes out the definition
+directly:
 
     S_ij   = scale * <q_i, k_j>                 (scale defaults to 1/sqrt(d))
     allowed(i, j) = (not causal) or kpos_j <= qpos_i      (global positions)
