@@ -239,6 +239,20 @@ def test_ffn_bwd_rejects_invalid(lib):
     assert _ffn_bwd(lib, rows=0, work_bytes=0, **none) == 0              # nothing to do
 
 
+def test_timing_families_documented_in_the_header_are_accepted(lib):
+    """Every kernel family the header lists can be read back (no records
+    here: zero launches, no GPU call), and an unknown one is rejected."""
+    text = open(HEADER).read()
+    block = text[text.index("kernel timing (diagnostics)"):text.index("ring_attn_timing_enable(on)")]
+    names = re.findall(r'"([a-z0-9_]+)"', block)
+    assert {"fwd_bf16", "bwd_dkv", "fwd_decode", "ffn_up", "ffn_bwd_gemm"} <= set(names)
+    n, ms = ctypes.c_int(-1), ctypes.c_double(-1.0)
+    for name in names:
+        assert lib.ring_attn_timing_read(name.encode(), ctypes.byref(n), ctypes.byref(ms)) == 0
+        assert n.value == 0 and ms.value == 0.0
+    assert lib.ring_attn_timing_read(b"no_such_family", ctypes.byref(n), ctypes.byref(ms)) == -1
+
+
 def test_emulator_rejects_bad_schedules(lib):
     d = _dims()
     pool = (ctypes.c_void_p * 2)(FAKE2.value, 0x300000)
