@@ -74,6 +74,7 @@ SMALL = [
     ("one key per split", 1, 2, 0, 128, 3, 70, 1, 1, 0.0),
     ("single split over the whole block", 1, 2, 2, 128, 2, 129, 1, 4096, 0.0),
     ("ten blocks of 64 keys", 1, 4, 2, 128, 2, 64, 10, 64, 0.0),
+    ("a single key, three blocks", 2, 4, 1, 64, 3, 1, 3, 0, 0.0),
 ]
 
 
