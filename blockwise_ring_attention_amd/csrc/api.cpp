@@ -261,7 +261,10 @@ int ra_check_ffn(int64_t rows, int d_model, int d_ff, int chunk_rows) {
                    d_model, d_ff);
   if (chunk_rows < 1) return ra_fail(RA_ERR_INVALID, "chunk_rows %d must be >= 1", chunk_rows);
   const int64_t chunk = std::min<int64_t>(chunk_rows, std::max<int64_t>(rows, 1));
-  if (((chunk + 255) / 256) * (int64_t)(std::max(d_model, d_ff) / 256) > 0x7fffffffLL)
+  // Largest grids: a product over a chunk, the weight-gradient products
+  // (d_ff x d_model tiles of 256) and the weight transposes (tiles of 64).
+  if (((chunk + 255) / 256) * (int64_t)(std::max(d_model, d_ff) / 256) > 0x7fffffffLL ||
+      (int64_t)(d_ff / 64) * (d_model / 64) > 0x7fffffffLL)
     return ra_fail(RA_ERR_INVALID, "problem too large for one launch");
   return RA_OK;
 }

@@ -212,6 +212,7 @@ def test_ffn_bwd_workspace_size(lib):
     assert ws(0, dm, dff, 64) > 0
     assert ws(10, 200, dff, 64) == -2
     assert ws(10, dm, dff, 0) == -1
+    assert ws(10, 1 << 22, 1 << 22, 64) == -1      # weight transposes beyond one grid
 
 
 def _ffn_bwd(lib, rows=300, dm=256, dff=512, chunk=128, work_bytes=1 << 30, **ptrs):
