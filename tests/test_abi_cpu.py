@@ -293,3 +293,14 @@ def test_bench_trace_overlap_report(tmp_path, capsys):
     assert out["copy_kernels"] == 2
     assert out["overlap_fraction"] == round(120 / 200, 4)
     assert out["copy_queues"] == ["2"] and out["attention_queues"] == ["1"]
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one member's share on one GPU: --gpus 2 exits with a
+    message and a non-zero status before touching any device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
