@@ -13,8 +13,9 @@
 // Both products are C = A B^T with A [M x K] and B [N x K] row-major, so both
 // MFMA operands are contiguous along K and come from 16-byte LDS reads of
 // swizzled rows.  gemm_tn_kernel: one 256 x 256 output tile per workgroup,
-// four waves of 128 x 128 (one wave per SIMD; the accumulators take 256
-// registers), K in steps of 64 staged through two LDS stages of
+// eight waves of 128 x 64 (two per SIMD, whose MFMA streams cover each
+// other's waits; the accumulators take 128 registers), K in steps of 64
+// staged through two LDS stages of
 // 2 x 256 x 64 bf16 filled by direct-to-LDS copies one step ahead.  Tiles
 // are ordered in groups of eight row tiles per XCD so that the workgroups
 // running together on one XCD share A and B tiles in its L2.  The epilogue
@@ -41,7 +42,7 @@ struct GemmCfg {
   static constexpr int ROWB = BK * 2;               // bytes per staged row
   static constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
   static constexpr int RPL = 1024 / ROWB;           // rows per 1 KiB copy
-  static constexpr int LPW = BM / RPL / 4;          // copies per wave per tile
+  static constexpr int LPW = BM / RPL / 8;          // copies per wave (8 waves) per tile
   static constexpr int TILEB = BM * ROWB;
   static constexpr int STAGEB = 2 * TILEB;          // A then B
   static constexpr int SMEM = NSTAGE * STAGEB > BM * OUT_ROWB ? NSTAGE * STAGEB : BM * OUT_ROWB;
@@ -68,8 +69,8 @@ __device__ __forceinline__ int gswz(int r) {
 // (the swizzles are XOR-linear over these row bits; gswz(RPL j) is 2 (j & 1)
 // for 64 columns and 0 for 32).  ld is a multiple of 64 elements, so that XOR
 // never reaches the row part of the offset.  Rows at or past `rows` are
-// clamped to rows - 1 (their products are never stored).  Wave w issues
-// copies LPW w .. LPW w + LPW - 1.
+// clamped to rows - 1 (their products are never stored).  Wave w (of 8)
+// issues copies LPW w .. LPW w + LPW - 1.
 template <int BK, int NSTAGE>
 struct StridedTileLoader {
   using C = GemmCfg<BK, NSTAGE>;
@@ -150,7 +151,7 @@ __device__ __forceinline__ float gelu_grad(float z) {
 enum { kEpiStore = 0, kEpiGelu = 1, kEpiAccF32 = 2 };
 
 template <int EPI, int BK, int NSTAGE>
-__global__ __launch_bounds__(256, 1) void gemm_tn_kernel(
+__global__ __launch_bounds__(512, 1) void gemm_tn_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ B, void* __restrict__ Cv, int M,
     int N, int K, int tiles_m, int tiles_n) {
   using G = GemmCfg<BK, NSTAGE>;
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_kernel(
   const int tm = first_m + (t % per_group) % gm;
   const int tn = (t % per_group) / gm;
   const int m0 = tm * BM, n0 = tn * BN;
-  const int wm = wave >> 1, wn = wave & 1;   // the wave's 128 x 128 quadrant
+  const int wm = wave >> 2, wn = wave & 3;   // the wave's 128 x 64 part
 
   const StridedTileLoader<BK, NSTAGE> loader(wave, lane, K);
   auto issue = [&](int kt) __attribute__((always_inline)) {
@@ -188,41 +189,41 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_kernel(
 #pragma unroll
   for (int ds = 0; ds < DS; ++ds) roff[ds] = l32 * ROWB + (((2 * ds + hl) ^ gswz<BK>(l32)) << 4);
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  // Fragments of one 16-wide K slice: a[i] rows 32 i .. of the wave's A
-  // quadrant, b[j] rows 32 j .. of its B quadrant; two sets, so the reads of
-  // the next slice run under the MFMAs of this one.
-  bf16x8 fa[2][4], fb[2][4];
+  // Fragments of one 16-wide K slice: a[i] rows 32 i .. of the wave's 128
+  // A rows, b[j] rows 32 j .. of its 64 B rows; two sets, so the reads of the
+  // next slice run under the MFMAs of this one.
+  bf16x8 fa[2][4], fb[2][2];
   auto read = [&](int set, int stage, int ds) __attribute__((always_inline)) {
     const char* As = smem + stage * G::STAGEB + wm * 128 * ROWB + roff[ds];
-    const char* Bs = smem + stage * G::STAGEB + G::TILEB + wn * 128 * ROWB + roff[ds];
+    const char* Bs = smem + stage * G::STAGEB + G::TILEB + wn * 64 * ROWB + roff[ds];
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[set][i] = *(const bf16x8*)(As + i * 32 * ROWB);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fb[set][j] = *(const bf16x8*)(Bs + j * 32 * ROWB);
+    for (int j = 0; j < 2; ++j) fb[set][j] = *(const bf16x8*)(Bs + j * 32 * ROWB);
   };
   // B fragments as the MFMA's first operand: lane l32 of acc[i][j] holds row
-  // 32 i + l32 of the quadrant, register r its column 32 j + 8 (r / 4) +
+  // 32 i + l32 of the wave's part, register r its column 32 j + 8 (r / 4) +
   // 4 (lane / 32) + r % 4, so four consecutive registers are four adjacent
   // columns of one row.
   auto mfmas = [&](int set, int first, int count) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = first; q < first + count; ++q)
-      acc[q >> 2][q & 3] = mfma32(fb[set][q & 3], fa[set][q >> 2], acc[q >> 2][q & 3]);
+      acc[q >> 1][q & 1] = mfma32(fb[set][q & 1], fa[set][q >> 1], acc[q >> 1][q & 1]);
   };
-  // One MFMA, then one LDS read, eight times; then the remaining MFMAs.
+  // One MFMA, then one LDS read, six times; then the remaining MFMAs.
   auto interleave8 = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 6; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
   };
 
   // Steps 0 .. PF-1 before the loop; step kt issues step kt + PF into the
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_kernel(
 #pragma unroll
     for (int ds = 0; ds + 1 < DS; ++ds) {
       read((ds + 1) & 1, stage, ds + 1);
-      mfmas(ds & 1, 0, 16);
+      mfmas(ds & 1, 0, 8);
       interleave8();
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_kernel(
     // the next step's copies, the barrier, and the next step's first-slice
     // reads under the other half.
     constexpr int last = (DS - 1) & 1;
-    mfmas(last, 0, 8);
+    mfmas(last, 0, 4);
     __builtin_amdgcn_sched_barrier(0);
     if (kt + 1 < nk) {
       // step kt+1 has landed; steps kt+2 .. kt+PF may stay in flight
@@ -259,7 +260,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_kernel(
       __syncthreads();
       read(last ^ 1, (kt + 1) % NSTAGE, 0);
     }
-    mfmas(last, 8, 8);
+    mfmas(last, 4, 4);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -271,24 +272,24 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_kernel(
     float* Cf = (float*)Cv;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      if (wn == half) {
+      if ((wn >> 1) == half) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
               const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                                acc[i][j][4 * g + 3]};
               const int row = wm * 128 + i * 32 + l32;
-              const int col = j * 32 + 8 * g + 4 * hl;
+              const int col = (wn & 1) * 64 + j * 32 + 8 * g + 4 * hl;
               *(f32x4*)(smem + row * OUT_ROWB + col * 4) = v;
             }
       }
       __syncthreads();
 #pragma unroll 4
-      for (int it = 0; it < BM * 128 / 4 / 256; ++it) {
-        const int id = it * 256 + tid;
+      for (int it = 0; it < BM * 128 / 4 / 512; ++it) {
+        const int id = it * 512 + tid;
         const int row = id >> 5, c = id & 31;   // 32 chunks of 4 columns per row
         const f32x4 v = *(const f32x4*)(smem + row * OUT_ROWB + c * 16);
         if (m0 + row < M) {
@@ -299,14 +300,14 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_kernel(
       __syncthreads();
     }
   } else {
-    // Each wave writes its quadrant (after the activation, as bf16) into
+    // Each wave writes its part (after the activation, as bf16) into
     // the LDS tile, four adjacent columns per 8-byte write; then the
     // workgroup stores the tile row by row, 16 bytes per lane.
     bf16* C = (bf16*)Cv;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           bf16x4 v;
@@ -317,13 +318,13 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_kernel(
             v[e] = (bf16)x;
           }
           const int row = wm * 128 + i * 32 + l32;
-          const int col = wn * 128 + j * 32 + 8 * g + 4 * hl;
+          const int col = wn * 64 + j * 32 + 8 * g + 4 * hl;
           *(bf16x4*)(smem + row * OUT_ROWB + col * 2) = v;
         }
     __syncthreads();
 #pragma unroll 4
-    for (int it = 0; it < BM * BN / 8 / 256; ++it) {
-      const int id = it * 256 + tid;
+    for (int it = 0; it < BM * BN / 8 / 512; ++it) {
+      const int id = it * 512 + tid;
       const int row = id >> 5, c = id & 31;   // 32 chunks of 8 columns per row
       const u32x4 v = *(const u32x4*)(smem + row * OUT_ROWB + c * 16);
       if (m0 + row < M) *(u32x4*)(C + (size_t)(m0 + row) * N + n0 + c * 8) = v;
@@ -416,7 +417,7 @@ hipError_t gemm_tn(const bf16* A, const bf16* B, void* C, int M, int N, int K,
                    hipStream_t stream) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
   hipLaunchKernelGGL((gemm_tn_kernel<EPI, kBK, kStages>), dim3((unsigned)(tiles_m * tiles_n)),
-                     dim3(256), 0, stream, A, B, C, M, N, K, tiles_m, tiles_n);
+                     dim3(512), 0, stream, A, B, C, M, N, K, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
