@@ -144,3 +144,48 @@ def test_decode_full_size_every_row(kv_heads):
     o_ref, lse_ref = _oracle(cfg, q, kvs)
     check("o_acc", o, o_ref, "bf16")
     check_lse("lse_acc", lse, lse_ref)
+
+
+def test_speculative_step_composes_with_the_causal_diagonal_step():
+    """A short run of draft rows: they attend to every cached key through the
+    decode step, then to their own new keys through the ordinary causal
+    diagonal ring step; together that is exact causal attention over the
+    cache and the draft (grouped key/value heads, d = 128)."""
+    from blockwise_ring_attention_amd.inputs import draw
+    dev = torch.device("cuda:0")
+    cfg = DecodeConfig(96, "draft", 2, 8, 128, 8, 1000, blocks=2, kv_heads=2)
+    q, kvs = draw_decode(cfg, seed=7)
+    kv_draft = torch.stack([draw(cfg, "k", cfg.blocks, 7, length=cfg.q_len),
+                            draw(cfg, "v", cfg.blocks, 7, length=cfg.q_len)], dim=0)
+    qd = q.to(dev)
+    o_acc = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    lse_acc = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    _lib.ring_attn_init_acc(o_acc, lse_acc)
+    for kv in kvs:
+        kvd = kv.to(dev)
+        kc = _lib.ring_attn_decode_chunk(qd, kvd)
+        S = _lib.ring_attn_decode_splits(qd, kvd, kc)
+        o_part = torch.empty((S,) + tuple(q.shape), dtype=torch.float32, device=dev)
+        lse_part = torch.empty((S,) + tuple(q.shape[:3]), dtype=torch.float32, device=dev)
+        _lib.ring_attn_fwd_decode(qd, kvd, kc, o_acc, lse_acc, o_part, lse_part)
+    # the draft block is the member's own block: ring step 0, causal diagonal
+    _lib.ring_attn_fwd(qd, kv_draft.to(dev), 2, 0, 3, True, 256, 64, o_acc, lse_acc)
+    torch.cuda.synchronize()
+
+    Lk, G = cfg.kv_len, cfg.heads // cfg.n_kv_heads
+    k_pos = np.concatenate([oracle.positions(0, Lk), oracle.positions(1, Lk),
+                            2 * Lk + np.arange(cfg.q_len)])
+    q_pos = 2 * Lk + np.arange(cfg.q_len)
+    o_ref = np.zeros(q.shape)
+    lse_ref = np.zeros(q.shape[:3])
+    for b in range(cfg.batch):
+        for kh in range(cfg.n_kv_heads):
+            k = torch.cat([kvs[0][0, b:b + 1, kh:kh + 1], kvs[1][0, b:b + 1, kh:kh + 1],
+                           kv_draft[0, b:b + 1, kh:kh + 1]], dim=2)
+            v = torch.cat([kvs[0][1, b:b + 1, kh:kh + 1], kvs[1][1, b:b + 1, kh:kh + 1],
+                           kv_draft[1, b:b + 1, kh:kh + 1]], dim=2)
+            ob, lb = oracle.attention(q[b:b + 1, kh * G:(kh + 1) * G], k, v, q_pos, k_pos, True)
+            o_ref[b, kh * G:(kh + 1) * G] = ob[0]
+            lse_ref[b, kh * G:(kh + 1) * G] = lb[0]
+    check("o_acc", o_acc.cpu(), o_ref, "bf16")
+    check_lse("lse_acc", lse_acc.cpu(), lse_ref)
