@@ -18,6 +18,14 @@
  *   memory.  All work is enqueued asynchronously on the given hipStream_t
  *   (passed as void*; NULL = the null stream); a device fault surfaces at the
  *   caller's next synchronisation.
+ * - Every compute entry point (ring_attn_init_acc, ring_attn_fwd,
+ *   ring_attn_fwd_decode, ring_attn_combine, ring_attn_finalize,
+ *   ring_attn_bwd_prep, ring_attn_bwd, ring_ffn_fwd, ring_ffn_bwd) only
+ *   launches kernels on the given stream: no allocation, no hipMemset, no
+ *   synchronisation, so a sequence of them may be captured into a HIP graph
+ *   and replayed.  Timing (ring_attn_timing_enable) records events and must
+ *   be off while capturing.  The ring emulator entry points create events
+ *   and use a second stream; they are not meant for capture.
  * - Layouts are dense row-major, no strides (H = ra_dims.heads query heads,
  *   Hkv = ra_dims.kv_heads key/value heads):
  *     q, dout          [B, H, Lq, d]        (dtype of ra_dims.dtype)
