@@ -15,6 +15,8 @@ What it computes
   Ring Attention with Blockwise Transformers, abstract), so the share of a
   ring member equals this definition restricted to the member's rows.
 * ``attention_grads``: the closed-form exact gradient of sum(dO * O).
+* ``attention_grads_at_keys``: the same dK / dV restricted to chosen keys,
+  for shares too long to hold dS whole.
 * ``ffn.feedforward``: the position-wise two-layer MLP GELU(x W1^T) W2^T
   that the blockwise feedforward computes chunk by chunk (Ring Attention
   with Blockwise Transformers, abstract: attention and the feedforward are
@@ -33,10 +35,10 @@ and value-linearity identities, finite differences for the gradients, torch
 fp64 autograd and SDPA as independent library routines, gradient sum
 identities, combine associativity / commutativity / identity.
 """
-from .exact import attention, attention_grads, positions
+from .exact import attention, attention_grads, attention_grads_at_keys, positions
 from .ffn import feedforward, feedforward_grad_magnitudes, feedforward_grads, gelu, gelu_grad
 from .ring import combine, block_partial, ring_share, ring_schedule
 
-__all__ = ["attention", "attention_grads", "positions", "combine",
+__all__ = ["attention", "attention_grads", "attention_grads_at_keys", "positions", "combine",
            "block_partial", "ring_share", "ring_schedule", "feedforward", "feedforward_grads",
            "feedforward_grad_magnitudes", "gelu", "gelu_grad"]

@@ -145,3 +145,57 @@ def attention_grads(q, k, v, do, q_pos, k_pos, causal: bool,
                 dk[b, kh] += sc * (ds.T @ q[b, h, r0:r1])
                 dv[b, kh] += p.T @ dot
     return dq, dk, dv, o, lse
+
+
+def attention_grads_at_keys(q, k, v, do, q_pos, k_pos, causal: bool, keys,
+                            scale: float | None = None, row_tile: int = 256):
+    """dK and dV of the chosen keys only (``keys``: indices into the key
+    axis), for shares whose full dS does not fit in memory.
+
+    The same closed form as ``attention_grads``.  First the log-sum-exp
+    LSE_i and delta_i = <dO_i, O_i> of every row (each row computed whole,
+    one tile of rows at a time); then, for each chosen key j,
+        P_ij = exp(S_ij - LSE_i),
+        dV_j = sum_i P_ij dO_i,
+        dK_j = scale * sum_i P_ij (<dO_i, v_j> - delta_i) q_i,
+    summed over the query heads that share key/value head of j.  Rows with
+    no allowed key contribute nothing.  Returns (dk, dv), float64
+    [B, Hkv, len(keys), d]."""
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    k_pos = np.asarray(k_pos, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.int64)
+    B, H, Lq, d = q.shape
+    Hkv = _check_heads(H, k)
+    sc = _scale(d, scale)
+    dk = np.zeros((B, Hkv, len(keys), k.shape[-1]))
+    dv = np.zeros((B, Hkv, len(keys), v.shape[-1]))
+    for b in range(B):
+        for h in range(H):
+            kh = _kv_head(h, H, Hkv)
+            lse = np.full(Lq, -np.inf)
+            delta = np.zeros(Lq)
+            for r0 in range(0, Lq, row_tile):       # every row's LSE and delta
+                r1 = min(Lq, r0 + row_tile)
+                s = _scores(q[b, h, r0:r1], k[b, kh], q_pos[r0:r1], k_pos, causal, sc)
+                m = s.max(axis=1)
+                live = np.isfinite(m)
+                m_safe = np.where(live, m, 0.0)
+                e = np.exp(s - m_safe[:, None])
+                l = np.where(live, e.sum(axis=1), 1.0)
+                ot = (e @ v[b, kh]) / l[:, None]
+                ot[~live] = 0.0
+                lse[r0:r1] = np.where(live, m_safe + np.log(l), -np.inf)
+                delta[r0:r1] = (do[b, h, r0:r1] * ot).sum(axis=1)
+            ks, vs, kp = k[b, kh][keys], v[b, kh][keys], k_pos[keys]
+            for r0 in range(0, Lq, row_tile):       # the chosen keys' columns
+                r1 = min(Lq, r0 + row_tile)
+                live = np.isfinite(lse[r0:r1])
+                s = _scores(q[b, h, r0:r1], ks, q_pos[r0:r1], kp, causal, sc)
+                p = np.exp(s - np.where(live, lse[r0:r1], 0.0)[:, None])
+                p[~live] = 0.0
+                dot = do[b, h, r0:r1]
+                ds = p * (dot @ vs.T - delta[r0:r1, None])
+                dk[b, kh] += sc * (ds.T @ q[b, h, r0:r1])
+                dv[b, kh] += p.T @ dot
+    return dk, dv

@@ -190,3 +190,44 @@ def test_shared_kv_heads_full_size():
         check(f"dk[{kb}] kvh{kh}", dev.dkv_pool[kb][0][:, [kh]], dk_ref, "bf16")
         check(f"dv[{kb}] kvh{kh}", dev.dkv_pool[kb][1][:, [kh]], dv_ref, "bf16")
     assert torch.isfinite(dev.dq_acc).all()
+
+
+def test_benchmark_training_share_full_size():
+    """The training share the benchmark times (rank 7 of a ring of 8, 16384
+    tokens per member, 32 heads of 128, bf16, seed 0), run as the benchmark
+    runs it (emulated ring with side-stream hops): dQ on sampled rows of two
+    heads; dK / dV of one head at keys on block and tile seams of every block,
+    whose gradients need every row of the share (the oracle takes each row's
+    log-sum-exp and delta from a full pass, then only those key columns)."""
+    from blockwise_ring_attention_amd.configs import scaled
+    cfg = scaled(CONFIGS[3], backward=True)
+    rank = cfg.ranks[0]
+    L = cfg.block_len
+    print("bench share: generating inputs", flush=True)
+    host = share.make_host_share(cfg, rank, seed=0, backward=True)
+    print("bench share: running forward + backward", flush=True)
+    dev = _run(host, side_stream=share.side_stream_for(torch.device("cuda:0")))
+    rng = np.random.default_rng(12)
+    rows = seam_rows(L, cfg.q_chunk, rng, 8)
+    heads = sorted(rng.choice(cfg.heads, size=2, replace=False).tolist())
+    print(f"bench share: oracle dq on {len(rows)} rows of heads {heads}", flush=True)
+    dq_ref, _ = _oracle_grads(host, heads=heads, rows=rows)
+    check("dq", dev.dq_acc[:, heads][:, :, rows], dq_ref, "bf16")
+
+    h = int(rng.integers(cfg.heads))
+    blocks = sorted(host.kv)
+    local = sorted({0, 63, 64, 255, 256, L - 65, L - 64, L - 1} |
+                   set(rng.choice(L, size=2, replace=False).tolist()))
+    keys = [b * L + j for b in blocks for j in local]
+    k = torch.cat([host.kv[b][0][:, [h]] for b in blocks], dim=2)
+    v = torch.cat([host.kv[b][1][:, [h]] for b in blocks], dim=2)
+    k_pos = np.concatenate([oracle.positions(b, L) for b in blocks])
+    print(f"bench share: oracle dk/dv of head {h} at {len(keys)} keys", flush=True)
+    dk_ref, dv_ref = oracle.attention_grads_at_keys(
+        host.q[:, [h]], k, v, host.dout[:, [h]], oracle.positions(rank, L), k_pos, True, keys)
+    for i, b in enumerate(blocks):
+        sel = slice(i * len(local), (i + 1) * len(local))
+        got = dev.dkv_pool[b][:, :, [h]][:, :, :, local].cpu()
+        check(f"dk[{b}] h{h}", got[0], dk_ref[:, :, sel], "bf16")
+        check(f"dv[{b}] h{h}", got[1], dv_ref[:, :, sel], "bf16")
+    assert torch.isfinite(dev.dq_acc).all()

@@ -117,3 +117,47 @@ def test_shared_kv_heads_autograd_fp64(kv_heads):
     np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12)
     np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12)
     np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal,kv_heads", [(True, 2), (False, 1), (True, 4)])
+def test_grads_at_chosen_keys_against_torch_autograd(causal, kv_heads):
+    """dK / dV of chosen keys (the routine used where the whole dS does not
+    fit) against torch fp64 autograd through SDPA with an explicit mask over
+    global positions: the rows of member 2 of a ring of blocks of 23 against
+    every key up to its own block (past blocks and the diagonal), several row
+    tiles with a ragged tail, keys at block seams and inside blocks."""
+    from oracle import attention_grads_at_keys
+    rng = np.random.default_rng(47 + kv_heads)
+    B, H, L, d, rank = 1, 4, 23, 16, 2
+    q, do = rng.standard_normal((B, H, L, d)), rng.standard_normal((B, H, L, d))
+    Lk = (rank + 1) * L
+    k, v = rng.standard_normal((B, kv_heads, Lk, d)), rng.standard_normal((B, kv_heads, Lk, d))
+    q_pos, k_pos = rank * L + np.arange(L), np.arange(Lk)
+    keys = [0, 5, L - 1, L, 2 * L - 1, 2 * L, 2 * L + 11, Lk - 1]
+    dk, dv = attention_grads_at_keys(q, k, v, do, q_pos, k_pos, causal, keys, row_tile=7)
+    assert dk.shape == (B, kv_heads, len(keys), d) and dv.shape == dk.shape
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    mask = torch.from_numpy(k_pos[None, :] <= q_pos[:, None]) if causal else None
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask,
+                                                          enable_gqa=True)
+    to.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(dk, tk.grad.numpy()[:, :, keys], atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy()[:, :, keys], atol=1e-12)
+
+
+def test_grads_at_chosen_keys_ignore_rows_with_no_visible_key():
+    """Causal rows placed before every key see nothing and must contribute
+    nothing (no NaN from their empty softmax)."""
+    from oracle import attention_grads_at_keys
+    rng = np.random.default_rng(53)
+    q, do = rng.standard_normal((1, 2, 12, 8)), rng.standard_normal((1, 2, 12, 8))
+    k, v = rng.standard_normal((1, 2, 10, 8)), rng.standard_normal((1, 2, 10, 8))
+    q_pos = np.array([-4, -1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9])
+    k_pos = np.arange(10)
+    keys = [0, 3, 9]
+    dk, dv = attention_grads_at_keys(q, k, v, do, q_pos, k_pos, True, keys, row_tile=5)
+    dk2, dv2 = attention_grads_at_keys(q[:, :, 2:], k, v, do[:, :, 2:], q_pos[2:], k_pos, True,
+                                       keys, row_tile=5)
+    assert np.isfinite(dk).all() and np.isfinite(dv).all()
+    np.testing.assert_allclose(dk, dk2, atol=1e-13)
+    np.testing.assert_allclose(dv, dv2, atol=1e-13)
