@@ -85,3 +85,22 @@ def test_planted_interleaved_kv_groups_are_caught(monkeypatch):
     monkeypatch.setattr(oa, "_kv_head", lambda h, H, Hkv: h % Hkv)
     with pytest.raises(AssertionError):
         pin(2)
+
+
+@pytest.mark.parametrize("slip", [_diag_excluded, _no_scale, _local_positions, _sign_flip])
+def test_planted_slip_fails_the_chosen_keys_pin(monkeypatch, slip):
+    """The chosen-keys gradient routine shares the score helper: each slip
+    there must also fail its autograd pin."""
+    from tests.test_oracle_grads import test_grads_at_chosen_keys_against_torch_autograd as pin
+    pin(True, 2)  # the unmodified oracle passes
+    monkeypatch.setattr(oa, "_scores", slip)
+    with pytest.raises(AssertionError):
+        pin(True, 2)
+
+
+def test_planted_interleaved_kv_groups_fail_the_chosen_keys_pin(monkeypatch):
+    from tests.test_oracle_grads import test_grads_at_chosen_keys_against_torch_autograd as pin
+    pin(True, 2)
+    monkeypatch.setattr(oa, "_kv_head", lambda h, H, Hkv: h % Hkv)
+    with pytest.raises(AssertionError):
+        pin(True, 2)
