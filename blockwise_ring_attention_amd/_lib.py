@@ -21,6 +21,8 @@ LIB_PATH = os.path.join(_HERE, "libringattn.so")
 
 RA_BF16, RA_FP32 = 0, 1
 RA_EMU_OVERLAP, RA_EMU_SERIALIZE = 0, 1
+# RA_DECODE_SCRATCH_BYTES: size of the library's decode scratch array
+DECODE_SCRATCH_BYTES = 16 << 20
 _ERR_NAMES = {-1: "invalid argument", -2: "unsupported", -3: "HIP error"}
 
 
@@ -59,6 +61,7 @@ _SIGS = {
     "ring_attn_decode_chunk": ([ctypes.POINTER(Dims)], _i),
     "ring_attn_decode_splits": ([ctypes.POINTER(Dims), _i], _i),
     "ring_attn_fwd_decode": ([_vp, _vp, _i, _vp, _vp, _vp, _vp, ctypes.POINTER(Dims), _vp], _i),
+    "ring_attn_fwd_decode_noalloc": ([_vp, _vp, _i, _vp, _vp, ctypes.POINTER(Dims), _vp], _i),
     "ring_ffn_fwd": ([_vp, _vp, _vp, _vp, _vp, ctypes.c_int64, _i, _i, _i, _vp], _i),
     "ring_ffn_bwd_workspace": ([ctypes.c_int64, _i, _i, _i], ctypes.c_int64),
     "ring_ffn_bwd": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64, ctypes.c_int64, _i, _i,
@@ -193,6 +196,22 @@ def ring_attn_fwd_decode(q, kv_block, k_chunk, o_acc, lse_acc, o_part, lse_part,
     _check(load().ring_attn_fwd_decode(_ptr(q), _ptr(kv_block), int(k_chunk), _ptr(o_acc),
                                        _ptr(lse_acc), _ptr(o_part), _ptr(lse_part),
                                        ctypes.byref(dm), _stream(stream)))
+
+
+def ring_attn_fwd_decode_noalloc(q, kv_block, k_chunk, o_acc, lse_acc, scale=0.0,
+                                 stream=None):
+    """ring_attn_fwd_decode with the split partials in the library's own
+    device scratch array (nothing allocated; calls on one GPU must not
+    overlap in time)."""
+    _need(kv_block, q.dtype, "kv_block")
+    for t, n in ((o_acc, "o_acc"), (lse_acc, "lse_acc")):
+        _need(t, torch.float32, n)
+    if tuple(o_acc.shape) != tuple(q.shape) or tuple(lse_acc.shape) != tuple(q.shape[:3]):
+        raise ValueError("o_acc / lse_acc do not match q")
+    dm = _decode_dims(q, kv_block, scale)
+    _check(load().ring_attn_fwd_decode_noalloc(_ptr(q), _ptr(kv_block), int(k_chunk),
+                                               _ptr(o_acc), _ptr(lse_acc), ctypes.byref(dm),
+                                               _stream(stream)))
 
 
 def ring_ffn_fwd(x, w1, w2, hidden, out, chunk_rows, stream=None):

@@ -299,6 +299,43 @@ int ra_decode_splits(const ra_shape& s, int k_chunk) {
   return (int)(((int64_t)s.Lk + k_chunk - 1) / k_chunk);
 }
 
+// Validation shared by the two decode entry points.  On RA_OK, *S is the
+// number of key splits, or 0 when the call has nothing to attend (the
+// accumulators are then left as they are).
+int ra_check_decode_call(const void* q, const void* kv_block, int k_chunk, const float* o_acc,
+                         const float* lse_acc, const ra_dims* dims, ra_shape* s, int* S) {
+  *S = 0;
+  int rc = ra_check_dims(dims, s);
+  if (rc) return rc;
+  if ((rc = ra_check_decode(*s))) return rc;
+  if (k_chunk < 1) return ra_fail(RA_ERR_INVALID, "k_chunk %d must be >= 1", k_chunk);
+  if ((rc = ra_check_fwd_buffers(q, kv_block, o_acc, lse_acc, *s))) return rc;
+  if (s->q_rows == 0 || s->Lk == 0) return RA_OK;  // nothing to attend: identity
+  const int n = ra_decode_splits(*s, k_chunk);
+  if (n > kDecodeMaxSplits)
+    return ra_fail(RA_ERR_INVALID, "k_chunk %d gives %d key splits (at most %d)", k_chunk, n,
+                   kDecodeMaxSplits);
+  if ((int64_t)s->B * s->Hkv * n > 0x7fffffffLL || s->q_rows * (s->D / 4) / 256 >= 0x7fffffffLL)
+    return ra_fail(RA_ERR_INVALID, "problem too large for one launch");
+  *S = n;
+  return RA_OK;
+}
+
+// The split kernel and the fold, with the partials in o_part / lse_part.
+int ra_decode_step(const void* q, const void* kv_block, int k_chunk, int S, float* o_acc,
+                   float* lse_acc, float* o_part, float* lse_part, const ra_shape& s,
+                   hipStream_t stream) {
+  ra_launch L{s.B, s.H, s.Lq, s.Lk, s.D, s.Hkv, s.scale, 0, 0, k_chunk, stream};
+  Timed t(kDecode, L.stream);
+  hipError_t e = ra_launch_decode_split(q, kv_block, o_part, lse_part, k_chunk, S, L);
+  t.done();
+  if (e != hipSuccess) return ra_hip_fail(e, "decode kernel launch");
+  Timed tf(kDecodeFold, L.stream);
+  e = ra_launch_decode_fold(o_acc, lse_acc, o_part, lse_part, s.q_rows, s.D, S, L.stream);
+  tf.done();
+  return e == hipSuccess ? RA_OK : ra_hip_fail(e, "decode fold kernel launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -466,18 +503,9 @@ int ring_attn_fwd_decode(const void* q, const void* kv_block, int k_chunk, float
                          float* lse_acc, float* o_part, float* lse_part, const ra_dims* dims,
                          void* stream) {
   ra_shape s;
-  int rc = ra_check_dims(dims, &s);
-  if (rc) return rc;
-  if ((rc = ra_check_decode(s))) return rc;
-  if (k_chunk < 1) return ra_fail(RA_ERR_INVALID, "k_chunk %d must be >= 1", k_chunk);
-  if ((rc = ra_check_fwd_buffers(q, kv_block, o_acc, lse_acc, s))) return rc;
-  if (s.q_rows == 0 || s.Lk == 0) return RA_OK;  // nothing to attend: identity
-  const int S = ra_decode_splits(s, k_chunk);
-  if (S > kDecodeMaxSplits)
-    return ra_fail(RA_ERR_INVALID, "k_chunk %d gives %d key splits (at most %d)", k_chunk, S,
-                   kDecodeMaxSplits);
-  if ((int64_t)s.B * s.Hkv * S > 0x7fffffffLL || s.q_rows * (s.D / 4) / 256 >= 0x7fffffffLL)
-    return ra_fail(RA_ERR_INVALID, "problem too large for one launch");
+  int S = 0;
+  int rc = ra_check_decode_call(q, kv_block, k_chunk, o_acc, lse_acc, dims, &s, &S);
+  if (rc || S == 0) return rc;
   if (!o_part || !lse_part) return ra_fail(RA_ERR_INVALID, "NULL tensor pointer");
   const size_t qb = (size_t)s.q_rows * s.D * s.elem;
   const size_t kvb = (size_t)2 * s.kv_rows * s.D * s.elem;
@@ -491,15 +519,37 @@ int ring_attn_fwd_decode(const void* q, const void* kv_block, int k_chunk, float
       return ra_fail(RA_ERR_INVALID, "o_part / lse_part overlap another buffer");
   if (overlaps(o_part, opb, lse_part, lpb))
     return ra_fail(RA_ERR_INVALID, "o_part overlaps lse_part");
-  ra_launch L{s.B, s.H, s.Lq, s.Lk, s.D, s.Hkv, s.scale, 0, 0, k_chunk, (hipStream_t)stream};
-  Timed t(kDecode, L.stream);
-  hipError_t e = ra_launch_decode_split(q, kv_block, o_part, lse_part, k_chunk, S, L);
-  t.done();
-  if (e != hipSuccess) return ra_hip_fail(e, "decode kernel launch");
-  Timed tf(kDecodeFold, L.stream);
-  e = ra_launch_decode_fold(o_acc, lse_acc, o_part, lse_part, s.q_rows, s.D, S, L.stream);
-  tf.done();
-  return e == hipSuccess ? RA_OK : ra_hip_fail(e, "decode fold kernel launch");
+  return ra_decode_step(q, kv_block, k_chunk, S, o_acc, lse_acc, o_part, lse_part, s,
+                        (hipStream_t)stream);
+}
+
+int ring_attn_fwd_decode_noalloc(const void* q, const void* kv_block, int k_chunk,
+                                 float* o_acc, float* lse_acc, const ra_dims* dims,
+                                 void* stream) {
+  ra_shape s;
+  int S = 0;
+  int rc = ra_check_decode_call(q, kv_block, k_chunk, o_acc, lse_acc, dims, &s, &S);
+  if (rc || S == 0) return rc;
+  // o_part [S, B, H, Lq, d] at the start of the array, lse_part [S, B, H, Lq]
+  // after it on a 256-byte boundary.
+  const uint64_t opb = (uint64_t)S * (uint64_t)s.q_rows * s.D * 4;
+  const uint64_t lp_off = (opb + 255) / 256 * 256;
+  const uint64_t need = lp_off + (uint64_t)S * (uint64_t)s.q_rows * 4;
+  if (need > (uint64_t)RA_DECODE_SCRATCH_BYTES)
+    return ra_fail(RA_ERR_INVALID,
+                   "the %d key splits of k_chunk %d need %llu bytes of partials, more than "
+                   "the %u of the library's scratch array; use a larger k_chunk or "
+                   "ring_attn_fwd_decode",
+                   S, k_chunk, (unsigned long long)need, (unsigned)RA_DECODE_SCRATCH_BYTES);
+  void* base = nullptr;
+  size_t bytes = 0;
+  hipError_t e = ra_decode_scratch(&base, &bytes);
+  if (e != hipSuccess) return ra_hip_fail(e, "decode scratch array address");
+  if (need > bytes) return ra_fail(RA_ERR_INVALID, "decode scratch array too small");
+  float* o_part = (float*)base;
+  float* lse_part = (float*)((char*)base + lp_off);
+  return ra_decode_step(q, kv_block, k_chunk, S, o_acc, lse_acc, o_part, lse_part, s,
+                        (hipStream_t)stream);
 }
 
 int ring_ffn_fwd(const void* x, const void* w1, const void* w2, void* hidden, void* out,

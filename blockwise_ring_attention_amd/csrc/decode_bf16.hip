@@ -26,9 +26,19 @@
 // through LDS at the end.
 #include <math.h>
 
+#include <mutex>
+
 #include "ra_common.h"
+#include "ring_attn.h"
 
 using namespace ra;
+
+// Split partials of ring_attn_fwd_decode_noalloc: a device-resident array,
+// one copy per GPU, that lives until the process ends.  Host code never uses
+// the name below as an address (on the host it is only a stand-in symbol);
+// ra_decode_scratch() looks up each device's own address once and hands
+// that out.
+static __device__ __align__(256) char scratch[RA_DECODE_SCRATCH_BYTES];
 
 namespace {
 
@@ -326,4 +336,28 @@ hipError_t ra_launch_decode_fold(float* o_acc, float* lse_acc, const float* o_pa
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+// Device address of this GPU's copy of `scratch`, looked up with
+// hipGetSymbolAddress on the first call made while that device is current
+// and kept for later calls.
+hipError_t ra_decode_scratch(void** ptr, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *bytes = RA_DECODE_SCRATCH_BYTES;
+  return hipSuccess;
 }

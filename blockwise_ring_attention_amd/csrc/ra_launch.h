@@ -23,6 +23,8 @@ hipError_t ra_launch_fwd_bf16(const void* q, const void* kv, float* o_acc,
 // ra_launch_decode_fold folds them, in split order, into (o_acc, lse_acc).
 hipError_t ra_launch_decode_split(const void* q, const void* kv, float* o_part, float* lse_part,
                                   int k_chunk, int splits, const ra_launch& a);
+// This device's copy of the decode scratch array (RA_DECODE_SCRATCH_BYTES).
+hipError_t ra_decode_scratch(void** ptr, size_t* bytes);
 hipError_t ra_launch_decode_fold(float* o_acc, float* lse_acc, const float* o_part,
                                  const float* lse_part, int64_t rows, int D, int splits,
                                  hipStream_t stream);

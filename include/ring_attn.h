@@ -15,12 +15,14 @@
  * ---------------------------------------
  * - All tensor pointers are DEVICE pointers on the current HIP device.  The
  *   caller allocates and frees every buffer; the library allocates no device
- *   memory.  All work is enqueued asynchronously on the given hipStream_t
+ *   memory (its only device storage is the fixed scratch array of
+ *   ring_attn_fwd_decode_noalloc, part of the loaded code object).  All work is enqueued asynchronously on the given hipStream_t
  *   (passed as void*; NULL = the null stream); a device fault surfaces at the
  *   caller's next synchronisation.
  * - Every compute entry point (ring_attn_init_acc, ring_attn_fwd,
- *   ring_attn_fwd_decode, ring_attn_combine, ring_attn_finalize,
- *   ring_attn_bwd_prep, ring_attn_bwd, ring_ffn_fwd, ring_ffn_bwd) only
+ *   ring_attn_fwd_decode, ring_attn_fwd_decode_noalloc, ring_attn_combine,
+ *   ring_attn_finalize, ring_attn_bwd_prep, ring_attn_bwd, ring_ffn_fwd,
+ *   ring_ffn_bwd) only
  *   launches kernels on the given stream: no allocation, no hipMemset, no
  *   synchronisation, so a sequence of them may be captured into a HIP graph
  *   and replayed.  Timing (ring_attn_timing_enable) records events and must
@@ -192,6 +194,28 @@ int ring_attn_decode_splits(const ra_dims* dims, int k_chunk);
 int ring_attn_fwd_decode(const void* q, const void* kv_block, int k_chunk,
                          float* o_acc, float* lse_acc, float* o_part,
                          float* lse_part, const ra_dims* dims, void* stream);
+
+/* The same decode-shaped step for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): identical to ring_attn_fwd_decode with the same k_chunk --
+ * same kernels, bitwise the same result -- except that the split partials
+ * live in a device-resident array of RA_DECODE_SCRATCH_BYTES bytes owned by
+ * the library (one copy per GPU, held from the first call on that GPU until
+ * the process ends).  It calls no allocating routine.  The partials need
+ *     align256(S * B * H * Lq * d * 4) + S * B * H * Lq * 4
+ * bytes with S = ceil(Lk / k_chunk); a call needing more returns
+ * RA_ERR_INVALID before anything is enqueued (take a larger k_chunk, or
+ * ring_attn_fwd_decode with caller-provided partials).  Every call on one
+ * GPU uses that GPU's one array: calls that may overlap in time on the same
+ * GPU (different streams, or different host threads) race and give
+ * undefined results; serialise them.  The array keeps the last call's
+ * contents; each call writes every partial it reads, so nothing needs
+ * clearing.  Other requirements and errors as for ring_attn_fwd_decode;
+ * RA_ERR_HIP if the array's address cannot be obtained on this device. */
+#define RA_DECODE_SCRATCH_BYTES (16u << 20)
+int ring_attn_fwd_decode_noalloc(const void* q, const void* kv_block,
+                                 int k_chunk, float* o_acc, float* lse_acc,
+                                 const ra_dims* dims, void* stream);
 
 /* ---- blockwise feedforward ----------------------------------------------
  * The method computes self-attention and the feedforward blockwise (Ring

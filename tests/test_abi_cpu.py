@@ -32,6 +32,7 @@ def test_header_declares_the_boundary():
               "ring_attn_finalize", "ring_attn_init_acc", "ring_attn_last_error",
               "ring_attn_version", "ring_emu_fwd", "ring_emu_bwd", "ring_attn_fwd_decode",
               "ring_attn_decode_chunk", "ring_attn_decode_splits", "ring_ffn_fwd",
+              "ring_attn_fwd_decode_noalloc",
               "ring_ffn_bwd", "ring_ffn_bwd_workspace"):
         assert n in names
     assert sorted(_lib.EXPORTS) == names, "binding and header disagree"
@@ -142,6 +143,44 @@ def test_decode_empty_calls_are_no_ops(lib):
     assert _decode(lib, _dims(heads=0, q_len=1), **nul) == 0
     # no keys: accumulators unchanged, nothing enqueued
     assert _decode(lib, _dims(q_len=1, kv_len=0), kv=None, op=None, lp=None) == 0
+
+
+def _decode_noalloc(lib, dims, kc=64, q=FAKE, kv=FAKE2, o=ctypes.c_void_p(0x10000000),
+                    lse=ctypes.c_void_p(0x20000000)):
+    return lib.ring_attn_fwd_decode_noalloc(q, kv, kc, o, lse,
+                                            ctypes.byref(dims) if dims is not None else None,
+                                            None)
+
+
+def test_decode_noalloc_limit_and_validation(lib):
+    """The allocation-free decode step validates like ring_attn_fwd_decode and
+    rejects, before touching the device, splits whose partials exceed the
+    library's scratch array."""
+    text = open(HEADER).read()
+    m = re.search(r"#define RA_DECODE_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.DECODE_SCRATCH_BYTES
+    d1 = _dims(q_len=1, kv_len=4096)
+    assert _decode_noalloc(lib, None) == -1
+    assert _decode_noalloc(lib, _dims(q_len=1, dtype=1)) == -2
+    assert _decode_noalloc(lib, _dims(heads=2, q_len=65)) == -2
+    assert _decode_noalloc(lib, d1, kc=0) == -1
+    assert _decode_noalloc(lib, d1, q=None) == -1
+    assert _decode_noalloc(lib, d1, o=ctypes.c_void_p(0x1000)) == -1   # o_acc aliases q
+    # 64 x 64 rows, 512 splits of 128 keys: 1 GiB of partials > 16 MiB
+    far = dict(q=ctypes.c_void_p(1 << 40), kv=ctypes.c_void_p(2 << 40),
+               o=ctypes.c_void_p(3 << 40), lse=ctypes.c_void_p(4 << 40))
+    big = _dims(batch=64, heads=64, q_len=1, kv_len=65536)
+    assert _decode_noalloc(lib, big, kc=128, **far) == -1
+    assert b"scratch" in lib.ring_attn_last_error()
+    # one split past the limit: S * rows * (4 d + 4) bytes
+    rows = 8 * 32                                   # B = 8, H = 32, Lq = 1
+    s_max = _lib.DECODE_SCRATCH_BYTES // (rows * 129 * 4)
+    over = _dims(batch=8, heads=32, q_len=1, kv_len=(s_max + 1) * 64)
+    assert _decode_noalloc(lib, over, kc=64, **far) == -1
+    assert b"scratch" in lib.ring_attn_last_error()
+    nul = dict(q=None, kv=None, o=None, lse=None)
+    assert _decode_noalloc(lib, _dims(q_len=0), **nul) == 0
+    assert _decode_noalloc(lib, _dims(q_len=1, kv_len=0), kv=None) == 0
 
 
 def test_decode_split_planning(lib):
