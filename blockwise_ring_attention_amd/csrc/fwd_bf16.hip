@@ -39,10 +39,14 @@
 // meet at one barrier per tile.
 //
 // Softmax.  The running max is kept in log2 units (scores scaled by
-// scale*log2(e), folded into the exponent's FMA).  The accumulators are
-// rescaled only when some row's max grows by more than 2^8; until then the
-// stale max is used, probabilities stay below 2^8, and the final
-// normalisation with the same max keeps the result exact.
+// scale*log2(e), folded into the exponent's FMA).  A tile's probabilities
+// are first taken against the running max as it stands, with no row max at
+// all; only when some lane's partial row sum exceeds 2^16 (some score rose
+// more than 16 above the max, or the first tile, whose sentinel max makes
+// the sum infinite) is the row max taken, the accumulators rescaled and the
+// tile's probabilities recomputed.  Every probability stays <= 2^16, and the
+// final normalisation with the same max keeps the result exact.  Row sums
+// add the fp32 probabilities in four independent chains.
 //
 // Causal seam.  For the diagonal block (query and key positions share the
 // block offset) key j is visible to query i iff j <= i; a workgroup only
@@ -63,7 +67,9 @@ using namespace ra;
 
 namespace {
 
-constexpr float kRescaleThresh = 8.0f;  // log2 units
+// A tile's probabilities are taken against the running max as it stands
+// while this lane's share of their sum stays at most kSumLimit.
+constexpr float kSumLimit = 65536.0f;
 
 template <int D, int BN, int NW>
 struct FwdCfg {
@@ -193,6 +199,24 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
   // value: KK*2*DD MFMAs with two transpose reads each; scores: DS*KK MFMAs
   // with one 16-byte read each.
   using Pipe = MfmaReadPipeline<KK * 2 * DD, 2, DS * KK, 1, 4>;
+  // s (raw scores) -> pb = bf16(exp2(s*c2 - m)); returns this lane's share of
+  // the row sum of the fp32 probabilities, added in four independent chains.
+  auto probs = [&]() __attribute__((always_inline)) -> float {
+    const float negm = -m;
+    float r[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      f32x16 p;  // not written back into s: s stays valid for the rescale path
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p[i] = exp2_fast(fmaf(s[kk][i], c2, negm));
+        r[i & 3] += p[i];
+      }
+      pb[kk][0] = to_bf16x8(p, 0);
+      pb[kk][1] = to_bf16x8(p, 1);
+    }
+    return (r[0] + r[1]) + (r[2] + r[3]);
+  };
   auto softmax = [&](int t) __attribute__((always_inline)) {  // s (raw scores of tile t) -> pb, m, lsum
     const int kt0 = t * BN;
     // (wave-uniform; made scalar so the mask is a skipped branch, not selects)
@@ -205,32 +229,26 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
           if (kj >= Lk || (diag && kj > qi)) s[kk][r] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    // Probabilities against the running max as it stands.  Only if some lane's
+    // sum exceeds kSumLimit (a score more than log2(kSumLimit) above the max,
+    // or the first tile, where the max is still the sentinel and the sum is
+    // infinite) is the row max taken, the accumulators rescaled and the
+    // probabilities recomputed.  Every probability stays <= kSumLimit.
+    float rs = probs();
+    if (__builtin_amdgcn_ballot_w64(!(rs <= kSumLimit))) {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
+      for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kk][r]);
-    mx = max_halves(mx) * c2;
-    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleThresh)) {
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kk][r]);
+      mx = max_halves(mx) * c2;
       const float mnew = fmaxf(m, mx);
       const float alpha = exp2_fast(m - mnew);
       m = mnew;
       lsum *= alpha;
 #pragma unroll
       for (int dd = 0; dd < DD; ++dd) oacc[dd] *= alpha;
-    }
-    const float negm = -m;
-    float rs = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      f32x16 p;  // not written back into s: s is dead until the next scores
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = exp2_fast(fmaf(s[kk][r], c2, negm));
-        rs += p[r];
-      }
-      pb[kk][0] = to_bf16x8(p, 0);
-      pb[kk][1] = to_bf16x8(p, 1);
+      rs = probs();
     }
     lsum += rs;
   };
