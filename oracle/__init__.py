@@ -36,9 +36,9 @@ fp64 autograd and SDPA as independent library routines, gradient sum
 identities, combine associativity / commutativity / identity.
 """
 from .exact import attention, attention_grads, attention_grads_at_keys, positions
-from .ffn import feedforward, feedforward_grad_magnitudes, feedforward_grads, gelu, gelu_grad
+from .ffn import feedforward, feedforward_grad_rss, feedforward_grads, gelu, gelu_grad
 from .ring import combine, block_partial, ring_share, ring_schedule
 
 __all__ = ["attention", "attention_grads", "attention_grads_at_keys", "positions", "combine",
            "block_partial", "ring_share", "ring_schedule", "feedforward", "feedforward_grads",
-           "feedforward_grad_magnitudes", "gelu", "gelu_grad"]
+           "feedforward_grad_rss", "gelu", "gelu_grad"]

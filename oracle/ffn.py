@@ -66,13 +66,28 @@ def feedforward_grads(x, w1, w2, dout):
     return dz @ w1, dz.T @ x, dout.T @ h
 
 
-def feedforward_grad_magnitudes(x, w1, w2, dout):
-    """Sums of the absolute values of the terms behind each gradient entry:
-    (|dZ| |W1|, |dZ|^T |x|, |dOut|^T |H|), float64, same shapes as
-    feedforward_grads.  An entry whose terms cancel has a small value but a
-    large sum of magnitudes; rounding each term by a relative e moves the
-    entry by at most e times this sum."""
+def gelu_grad2(z):
+    """d^2 GELU / dz^2 = phi(z) (2 - z^2)."""
+    z = np.asarray(z, dtype=np.float64)
+    return np.exp(-0.5 * z * z) / np.sqrt(2.0 * np.pi) * (2.0 - z * z)
+
+
+def feedforward_grad_rss(x, w1, w2, dout):
+    """Error scale of each gradient entry: the root-sum-square, over the terms
+    behind the entry, of each term's first-order sensitivity to relative
+    perturbations of the intermediates it is formed from (dH, Z and dZ for
+    the terms dZ * W1 of dx and dZ * x of dW1, where dZ = dH GELU'(Z);
+    Z and H = GELU(Z) for the terms dOut * H of dW2):
+        dx, dW1:  |dH| (2 |GELU'(z)| + |z GELU''(z)|) times |W1| or |x|
+        dW2:      |dOut| (|GELU(z)| + |z GELU'(z)|)
+    Float64, same shapes as feedforward_grads.  If each intermediate carries
+    an independent relative error of RMS e, an entry's error has RMS at most
+    about e times this value, however much the terms cancel (and a term whose
+    own value vanishes, GELU'(z) = 0, still has its sensitivity to z)."""
     x, w1, w2, dout = _as64(x), _as64(w1), _as64(w2), _as64(dout)
     z = x @ w1.T
-    dz = np.abs((dout @ w2) * gelu_grad(z))
-    return dz @ np.abs(w1), dz.T @ np.abs(x), np.abs(dout).T @ np.abs(gelu(z))
+    sens = np.abs(dout @ w2) * (2.0 * np.abs(gelu_grad(z)) + np.abs(z * gelu_grad2(z)))
+    s2 = sens ** 2
+    hs = np.abs(gelu(z)) + np.abs(z * gelu_grad(z))
+    return (np.sqrt(s2 @ (w1 * w1)), np.sqrt(s2.T @ (x * x)),
+            np.sqrt((dout * dout).T @ (hs * hs)))

@@ -7,7 +7,7 @@ import torch
 import oracle
 from blockwise_ring_attention_amd import _lib, share
 from blockwise_ring_attention_amd.configs import CONFIGS, ShareConfig
-from tests._gates import check, seam_rows
+from tests._gates import check, seam_rows, tile_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -106,9 +106,24 @@ def test_travelling_partial_accumulates():
         check(f"dv[{kb}]", got[1], dv_ref, "bf16")
 
 
+def _dq_every_tile(host, dev, rng, seams):
+    """dQ against the oracle on one random row of every 256-row query tile
+    of every head (plus the seam rows): every workgroup of the dQ launches
+    has a row checked."""
+    cfg = host.cfg
+    got, want = [], []
+    for h in range(cfg.heads):
+        rows = tile_rows(cfg.block_len, 256, rng, seams)
+        dq_ref, _ = _oracle_grads(host, heads=[h], rows=rows)
+        got.append(dev.dq_acc[:, [h]][:, :, rows].cpu())
+        want.append(dq_ref)
+    check("dq", torch.cat(got, dim=2), np.concatenate(want, axis=2), "bf16")
+
+
 def test_cfg4_full_size():
-    """Training share at full size: dQ on sampled rows of every head, dK/dV
-    of every block on two sampled heads (their gradients need every row)."""
+    """Training share at full size: dQ on one row of every query tile of
+    every head (plus seams), dK/dV of every block on two sampled heads
+    (their gradients need every row)."""
     cfg = CONFIGS[4]
     rank = cfg.ranks[0]
     print("cfg4: generating inputs", flush=True)
@@ -116,12 +131,10 @@ def test_cfg4_full_size():
     print("cfg4: running forward + backward share", flush=True)
     dev = _run(host, side_stream=torch.cuda.Stream())
     rng = np.random.default_rng(4)
-    rows = seam_rows(cfg.block_len, cfg.q_chunk, rng, 16)
-    heads = sorted(rng.choice(cfg.heads, size=4, replace=False).tolist())
-    print(f"cfg4: oracle dq on {len(rows)} rows x {len(heads)} heads", flush=True)
-    dq_ref, _ = _oracle_grads(host, heads=heads, rows=rows)
-    check("dq", dev.dq_acc[:, heads][:, :, rows], dq_ref, "bf16")
-    for h in heads[:2]:
+    print(f"cfg4: oracle dq on every tile of {cfg.heads} heads", flush=True)
+    _dq_every_tile(host, dev, rng, seam_rows(cfg.block_len, cfg.q_chunk, rng, 0))
+    heads = sorted(rng.choice(cfg.heads, size=2, replace=False).tolist())
+    for h in heads:
         print(f"cfg4: oracle dk/dv head {h}", flush=True)
         _, per_block = _oracle_grads(host, heads=[h])
         for kb, (dk_ref, dv_ref) in per_block.items():
@@ -195,10 +208,11 @@ def test_shared_kv_heads_full_size():
 def test_benchmark_training_share_full_size():
     """The training share the benchmark times (rank 7 of a ring of 8, 16384
     tokens per member, 32 heads of 128, bf16, seed 0), run as the benchmark
-    runs it (emulated ring with side-stream hops): dQ on sampled rows of two
-    heads; dK / dV of one head at keys on block and tile seams of every block,
-    whose gradients need every row of the share (the oracle takes each row's
-    log-sum-exp and delta from a full pass, then only those key columns)."""
+    runs it (emulated ring with side-stream hops): dQ on one row of every
+    query tile of every head; dK / dV of one head at keys on block and tile
+    seams of every block, whose gradients need every row of the share (the
+    oracle takes each row's log-sum-exp and delta from a full pass, then
+    only those key columns)."""
     from blockwise_ring_attention_amd.configs import scaled
     cfg = scaled(CONFIGS[3], backward=True)
     rank = cfg.ranks[0]
@@ -208,11 +222,8 @@ def test_benchmark_training_share_full_size():
     print("bench share: running forward + backward", flush=True)
     dev = _run(host, side_stream=share.side_stream_for(torch.device("cuda:0")))
     rng = np.random.default_rng(12)
-    rows = seam_rows(L, cfg.q_chunk, rng, 8)
-    heads = sorted(rng.choice(cfg.heads, size=2, replace=False).tolist())
-    print(f"bench share: oracle dq on {len(rows)} rows of heads {heads}", flush=True)
-    dq_ref, _ = _oracle_grads(host, heads=heads, rows=rows)
-    check("dq", dev.dq_acc[:, heads][:, :, rows], dq_ref, "bf16")
+    print(f"bench share: oracle dq on every tile of {cfg.heads} heads", flush=True)
+    _dq_every_tile(host, dev, rng, [0, 1, L - 1])
 
     h = int(rng.integers(cfg.heads))
     blocks = sorted(host.kv)

@@ -12,7 +12,7 @@ import oracle
 from blockwise_ring_attention_amd import _lib
 from blockwise_ring_attention_amd.configs import FFN_CONFIGS, FfnConfig
 from blockwise_ring_attention_amd.inputs import draw_ffn, draw_ffn_dout
-from tests._gates import check, check_sum
+from tests._gates import check, check_rss
 
 pytestmark = pytest.mark.gpu
 
@@ -106,10 +106,10 @@ def test_ffn_backward_small_elementwise(case):
     dout = draw_ffn_dout(cfg, seed=5)
     dx, dw1, dw2 = _run_bwd(x, w1, w2, dout, chunk)
     rdx, rdw1, rdw2 = oracle.feedforward_grads(x, w1, w2, dout)
-    mdx, mdw1, mdw2 = oracle.feedforward_grad_magnitudes(x, w1, w2, dout)
-    check_sum("dx", dx, rdx, mdx)
-    check_sum("dw1", dw1, rdw1, mdw1)
-    check_sum("dw2", dw2, rdw2, mdw2)
+    mdx, mdw1, mdw2 = oracle.feedforward_grad_rss(x, w1, w2, dout)
+    check_rss("dx", dx, rdx, mdx)
+    check_rss("dw1", dw1, rdw1, mdw1)
+    check_rss("dw2", dw2, rdw2, mdw2)
 
 
 def test_ffn_backward_accumulates_weight_gradients():
@@ -141,12 +141,12 @@ def test_ffn_backward_full_size_sampled():
     rows = np.array(sorted({0, 255, 256, cfg.chunk_rows - 1, cfg.chunk_rows, cfg.rows - 1}
                            | set(rng.choice(cfg.rows, size=12, replace=False).tolist())))
     rdx, _, _ = oracle.feedforward_grads(x[rows], w1, w2, dout[rows])
-    mdx, _, _ = oracle.feedforward_grad_magnitudes(x[rows], w1, w2, dout[rows])
-    check_sum("dx", dx[rows], rdx, mdx)
+    mdx, _, _ = oracle.feedforward_grad_rss(x[rows], w1, w2, dout[rows])
+    check_rss("dx", dx[rows], rdx, mdx)
     fs = np.array(sorted({0, 255, 256, cfg.d_ff - 1} |
                          set(rng.choice(cfg.d_ff, size=8, replace=False).tolist())))
     _, r1, r2 = oracle.feedforward_grads(x, w1[fs], w2[:, fs], dout)
-    _, m1, m2 = oracle.feedforward_grad_magnitudes(x, w1[fs], w2[:, fs], dout)
+    _, m1, m2 = oracle.feedforward_grad_rss(x, w1[fs], w2[:, fs], dout)
     sel = torch.from_numpy(fs).cuda()
-    check_sum("dw1", dw1[sel].cpu(), r1, m1)
-    check_sum("dw2", dw2[:, sel].cpu(), r2, m2)
+    check_rss("dw1", dw1[sel].cpu(), r1, m1)
+    check_rss("dw2", dw2[:, sel].cpu(), r2, m2)

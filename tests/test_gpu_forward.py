@@ -9,7 +9,7 @@ import torch
 import oracle
 from blockwise_ring_attention_amd import _lib, share
 from blockwise_ring_attention_amd.configs import CONFIGS, ShareConfig, Dist, scaled
-from tests._gates import check, check_lse, oracle_rows, seam_rows
+from tests._gates import check, check_lse, oracle_rows, oracle_rows_per_head, seam_rows, tile_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -169,10 +169,26 @@ def test_combine_kernel_algebra():
         np.testing.assert_allclose(l.cpu().numpy()[fin], ref[1][fin], atol=1e-5)
 
 
+def _tile_parity(host, dev, out, tile, rng, seams):
+    """Compare one row of every query tile of every head (plus seam rows) with
+    the oracle: every workgroup the launch ran has a row checked."""
+    cfg = host.cfg
+    rows_of = {h: tile_rows(cfg.block_len, tile, rng, seams) for h in range(cfg.heads)}
+    ref = oracle_rows_per_head(host, rows_of)
+    for name, got_all in (("o_acc", dev.o_acc), ("o (bf16)", out)):
+        got = torch.cat([got_all[:, h][:, rows_of[h]] for h in range(cfg.heads)], dim=1)
+        want = np.concatenate([ref[h][0] for h in range(cfg.heads)], axis=1)
+        check(name, got, want, "bf16")
+    got = torch.cat([dev.lse_acc[:, h][:, rows_of[h]] for h in range(cfg.heads)], dim=1)
+    check_lse("lse", got, np.concatenate([ref[h][1] for h in range(cfg.heads)], axis=1))
+    return sum(len(r) for r in rows_of.values())
+
+
 @pytest.mark.parametrize("cfg_id", [2, 3, 5])
-def test_full_size_sampled_rows(cfg_id):
-    """Full-size workloads at the benchmark's launch configuration, compared
-    with the oracle on seam and random rows of a subset of heads."""
+def test_full_size_every_tile(cfg_id):
+    """Full-size workloads at the benchmark's launch configuration (256-row
+    query tiles), compared with the oracle on one random row of every tile of
+    every head, plus block and chunk seam rows."""
     cfg = CONFIGS[cfg_id]
     rank = cfg.ranks[0]
     print(f"cfg{cfg_id} rank {rank}: generating inputs", flush=True)
@@ -180,16 +196,57 @@ def test_full_size_sampled_rows(cfg_id):
     print(f"cfg{cfg_id}: running share", flush=True)
     dev, out = _run(host)
     rng = np.random.default_rng(cfg_id)
-    rows = seam_rows(cfg.block_len, cfg.q_chunk, rng, 24)
-    heads = sorted(rng.choice(cfg.heads, size=min(6, cfg.heads), replace=False).tolist())
-    print(f"cfg{cfg_id}: oracle on {len(rows)} rows x {len(heads)} heads", flush=True)
-    o_ref, lse_ref = oracle_rows(host, heads, rows)
-    o_acc = dev.o_acc[:, heads][:, :, rows]
-    check("o_acc", o_acc, o_ref, "bf16")
-    check("o (bf16)", out[:, heads][:, :, rows], o_ref, "bf16")
-    check_lse("lse", dev.lse_acc[:, heads][:, :, rows], lse_ref)
-    # every row finite, and every LSE at least the largest single score
+    seams = seam_rows(cfg.block_len, cfg.q_chunk, rng, 0)
+    n = _tile_parity(host, dev, out, 256, rng, seams)
+    print(f"cfg{cfg_id}: {n} rows checked over {cfg.heads} heads x batch {cfg.batch}", flush=True)
     assert torch.isfinite(dev.o_acc).all() and torch.isfinite(dev.lse_acc).all()
+
+
+@pytest.mark.parametrize("fault", ["dropped", "duplicated", "wrong block"])
+def test_full_size_ring_faults_fail_the_gates(fault):
+    """Negative controls at the 16384-query causal share (rank 7 of 8): a ring
+    step that loses a past block, folds one twice, or receives block kb + 1 in
+    place of kb must fail the parity gates (on o the 2e-2 absolute term alone
+    would not notice: o has a standard deviation of about 1.3e-3 here; the
+    relative Frobenius guard and the LSE gate do).  The untouched schedule
+    passes the same gates on the same rows.  A wrong cross-chunk combine can
+    leave attention quietly incorrect (darcstar commentary), so the gates
+    must see it."""
+    cfg = CONFIGS[3]
+    rank, N = cfg.ranks[0], cfg.ring_size
+    print(f"faults ({fault}): generating inputs", flush=True)
+    host = share.make_host_share(cfg, rank)
+    q = host.q.cuda()
+    kvd = {b: t.cuda() for b, t in host.kv.items()}
+    victim = 3                       # a past block
+    rng = np.random.default_rng(31)
+    heads = [0, 17]
+    rows_of = {h: tile_rows(cfg.block_len, 512, rng) for h in heads}
+    ref = oracle_rows_per_head(host, rows_of)
+
+    def run(faulty):
+        o = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+        _lib.ring_attn_init_acc(o, lse)
+        for s in range(N):
+            kb = (rank - s) % N
+            blocks = [kb]
+            if faulty and kb == victim:
+                blocks = {"dropped": [], "duplicated": [kb, kb], "wrong block": [kb + 1]}[fault]
+            for b in blocks:
+                _lib.ring_attn_fwd(q, kvd[b], rank, s, N, True, cfg.q_chunk, cfg.k_chunk, o, lse)
+        torch.cuda.synchronize()
+        return o, lse
+
+    def gates(o, lse):
+        for h in heads:
+            check(f"o h{h}", o[:, h][:, rows_of[h]], ref[h][0], "bf16")
+            check_lse(f"lse h{h}", lse[:, h][:, rows_of[h]], ref[h][1])
+
+    gates(*run(False))
+    print(f"faults ({fault}): faulty schedule", flush=True)
+    with pytest.raises(AssertionError, match="rel Frobenius|LSE"):
+        gates(*run(True))
 
 
 @pytest.mark.parametrize("kv_heads,dtype", [(1, "bf16"), (2, "bf16"), (2, "fp32")])

@@ -239,24 +239,81 @@ def test_planted_weight_gradient_transposed_is_caught():
     assert not _pin_grads_autograd(slipped, d_model=12, d_ff=12)
 
 
-def test_grad_magnitudes_bound_each_gradient():
-    """The magnitude sums are, entry by entry, the sums of |terms| (checked by
-    brute force), and therefore bound the gradients themselves."""
-    from oracle import feedforward_grad_magnitudes
+def test_grad_rss_is_the_root_sum_square_of_the_term_sensitivities():
+    """Entry by entry (scalar loops, math.fsum): the root-sum-square over the
+    entry's terms of each term's sensitivity |dH| (2|GELU'| + |z GELU''|)
+    |w1 or x| (dx, dW1) or |dOut| (|GELU| + |z GELU'|) (dW2), with GELU''
+    the derivative of the printed-table-pinned GELU' taken by central
+    differences; never below the largest term itself."""
+    from oracle import feedforward_grad_rss
     rng = np.random.default_rng(14)
     x, w1, w2 = _rand(rng, 6, 4, 5)
+    x[0, 0] = -0.75 * 2.0  # some pre-activations near GELU'(z) = 0
     dout = rng.standard_normal((6, 4))
-    dx, dw1, dw2 = feedforward_grads(x, w1, w2, dout)
-    mdx, mdw1, mdw2 = feedforward_grad_magnitudes(x, w1, w2, dout)
+    sdx, sdw1, sdw2 = feedforward_grad_rss(x, w1, w2, dout)
     z = x @ w1.T
-    dz = (dout @ w2) * gelu_grad(z)
-    h = gelu(z)
-    for r in range(6):
-        for c in range(4):
-            assert abs(mdx[r, c] - math.fsum(abs(dz[r, f] * w1[f, c]) for f in range(5))) < 1e-12
-    for f in range(5):
-        for c in range(4):
-            assert abs(mdw1[f, c] - math.fsum(abs(dz[r, f] * x[r, c]) for r in range(6))) < 1e-12
-            assert abs(mdw2[c, f] - math.fsum(abs(dout[r, c] * h[r, f]) for r in range(6))) < 1e-12
-    for g, m in ((dx, mdx), (dw1, mdw1), (dw2, mdw2)):
-        assert (np.abs(g) <= m + 1e-12).all()
+    h = 1e-5
+    def g2(v):
+        return (float(gelu_grad(v + h)) - float(gelu_grad(v - h))) / (2 * h)
+    dh = [[math.fsum(dout[r, c] * w2[c, f] for c in range(4)) for f in range(5)] for r in range(6)]
+    sens = [[abs(dh[r][f]) * (2 * abs(float(gelu_grad(z[r, f]))) + abs(z[r, f] * g2(z[r, f])))
+             for f in range(5)] for r in range(6)]
+    hs = [[abs(float(gelu(z[r, f]))) + abs(z[r, f] * float(gelu_grad(z[r, f]))) for f in range(5)]
+          for r in range(6)]
+    cases = {
+        "dx": (sdx, [[[sens[r][f] * abs(w1[f, c]) for f in range(5)] for c in range(4)] for r in range(6)]),
+        "dw1": (sdw1, [[[sens[r][f] * abs(x[r, c]) for r in range(6)] for c in range(4)] for f in range(5)]),
+        "dw2": (sdw2, [[[abs(dout[r, c]) * hs[r][f] for r in range(6)] for f in range(5)] for c in range(4)]),
+    }
+    dx, dw1, dw2 = feedforward_grads(x, w1, w2, dout)
+    terms_max = {"dx": np.abs(dx), "dw1": np.abs(dw1), "dw2": np.abs(dw2)}
+    for name, (got, t) in cases.items():
+        for i, row in enumerate(t):
+            for j, ts in enumerate(row):
+                want = math.sqrt(math.fsum(v * v for v in ts))
+                assert abs(got[i, j] - want) <= 1e-7 * max(1.0, want), (name, i, j)
+    # each term's sensitivity is at least its magnitude, so the scale is at
+    # least |g| / sqrt(number of terms)
+    for name, n in (("dx", 5), ("dw1", 6), ("dw2", 6)):
+        assert (cases[name][0] * np.sqrt(n) + 1e-12 >= terms_max[name]).all()
+
+
+def test_rss_gate_passes_bf16_rounding_and_catches_a_one_row_slip():
+    """The feedforward-gradient gate, |g - ref| <= 1e-2 scale + floor, on the
+    CPU: gradients formed the way the kernels form them (bf16 operands, bf16
+    Z, dH, dZ and H, fp32 products) pass it, for many rows and for one, while
+    the same gradients with one row of dW1 off by 5 % of rms(dW1) fail it (a
+    slip that the relative Frobenius guard alone does not see)."""
+    import torch
+    from oracle import feedforward_grad_rss
+    from tests._gates import check_rss
+    rng = np.random.default_rng(3)
+    rows, dm, dff = 384, 128, 256
+    def bf(a):
+        return torch.from_numpy(np.asarray(a, dtype=np.float32)).to(torch.bfloat16).double().numpy()
+    x = bf(rng.standard_normal((rows, dm)))
+    w1 = bf(rng.standard_normal((dff, dm)) / np.sqrt(dm))
+    w2 = bf(rng.standard_normal((dm, dff)) / np.sqrt(dff))
+    dout = bf(rng.standard_normal((rows, dm)))
+    zb = bf((x @ w1.T).astype(np.float32))
+    dzb = bf(bf((dout @ w2).astype(np.float32)) * gelu_grad(zb))
+    hb = bf(gelu(zb))
+    got = [(dzb @ w1).astype(np.float32), (dzb.T @ x).astype(np.float32),
+           (dout.T @ hb).astype(np.float32)]
+    ref = feedforward_grads(x, w1, w2, dout)
+    rss = feedforward_grad_rss(x, w1, w2, dout)
+    for name, g, r, q in zip(("dx", "dw1", "dw2"), got, ref, rss):
+        check_rss(name, g, r, q)
+    one = slice(0, 1)
+    r1 = feedforward_grads(x[one], w1, w2, dout[one])
+    q1 = feedforward_grad_rss(x[one], w1, w2, dout[one])
+    g1 = [(dzb[one] @ w1).astype(np.float32), (dzb[one].T @ x[one]).astype(np.float32),
+          (dout[one].T @ hb[one]).astype(np.float32)]
+    for name, g, r, q in zip(("dx", "dw1", "dw2"), g1, r1, q1):
+        check_rss(name + " one row", g, r, q)
+    slipped = got[1].copy()
+    slipped[7] += 0.05 * np.sqrt((ref[1] ** 2).mean())
+    rel_f = np.linalg.norm(slipped - ref[1]) / np.linalg.norm(ref[1])
+    assert rel_f < 1e-2, "the slip must be invisible to the Frobenius guard"
+    with pytest.raises(AssertionError):
+        check_rss("dw1", slipped, ref[1], rss[1])
