@@ -65,6 +65,11 @@ def _parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (a known amount of "
                          "HBM traffic, to scale the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--config", type=int, default=3,
+                    help="attention workload: 3 (default) the 16384-query causal share with "
+                         "its backward; 2 the non-causal share (forward); 4 the 8192-token "
+                         "training share (forward + backward); 5 the million-token share "
+                         "(forward)")
     ap.add_argument("--kv-heads", type=int, default=0,
                     help="key/value heads shared by groups of the 32 query heads (MQA / GQA); "
                          "0 (default): 32, ordinary multi-head attention")
@@ -176,51 +181,108 @@ def _measured_mfma_util(family):
     return None if p is None else p[1].get("mfma_util_pct")
 
 
-def _cpu_baseline(host, cfg, rank, target_s):
-    """The fp64 oracle, as it stands, on a bounded sample of the same share:
-    the last rows of some heads (rows that see every past block and nearly
-    all of the diagonal block), forward + gradients."""
+# State a forked oracle worker inherits (set just before the pool forks).
+_ORACLE_POOL_STATE = {}
+
+
+def _oracle_pool_init():
+    """Pool worker: one BLAS thread and one torch thread per process."""
+    import torch
+    from threadpoolctl import threadpool_limits
+    torch.set_num_threads(1)
+    _ORACLE_POOL_STATE["limits"] = threadpool_limits(1)
+
+
+def _oracle_task(task):
+    """The fp64 oracle on one slice of the share: head h, query rows
+    [r0, r0 + n), against every key block the member sees; forward and, for
+    training shares, the gradients.  Returns (unmasked pairs, seconds)."""
     import numpy as np
     import torch
 
     import oracle
+    st = _ORACLE_POOL_STATE
+    host, cfg, rank, backward, k_pos = (st["host"], st["cfg"], st["rank"], st["backward"],
+                                        st["k_pos"])
+    h, r0, n = task
+    blocks = sorted(host.kv)
+    t0 = time.perf_counter()
+    kh = oracle.exact._kv_head(h, cfg.heads, cfg.n_kv_heads)
+    k = torch.cat([host.kv[b][0][:, kh:kh + 1] for b in blocks], dim=2)
+    v = torch.cat([host.kv[b][1][:, kh:kh + 1] for b in blocks], dim=2)
+    rows = np.arange(r0, r0 + n)
+    q_pos = oracle.positions(rank, cfg.block_len)[rows]
+    q = host.q[:, h:h + 1, rows]
+    if backward:
+        oracle.attention_grads(q, k, v, host.dout[:, h:h + 1, rows], q_pos, k_pos, cfg.causal)
+    else:
+        oracle.attention(q, k, v, q_pos, k_pos, cfg.causal)
+    dt = time.perf_counter() - t0
+    pairs = int(sum(int((k_pos <= p).sum()) if cfg.causal else len(k_pos) for p in q_pos))
+    return pairs * cfg.batch, dt
 
-    cores = _oracle_threads()
+
+def _cpu_share():
+    """CPUs this process may use, capped at 16: the host CPU share of one GPU."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _cpu_baseline(host, cfg, rank, backward, target_s):
+    """The fp64 oracle, as it stands, on a bounded sample of the same share,
+    timed on the host: a pool of P processes (P = the CPU share, one BLAS
+    thread each) works through (head, 256-row tile) slices, the last tiles
+    of every head first (rows that see every key block).  One round of P
+    slices sizes the sample; then enough rounds for about target_s seconds
+    are timed.  Call before anything initialises the GPU: the pool forks."""
+    import multiprocessing as mp
+
+    import numpy as np
+
+    import oracle
     L = cfg.block_len
     blocks = sorted(host.kv)
-    k_pos = np.concatenate([oracle.positions(b, L) for b in blocks])
-
-    def run(heads, nrows):
-        rows = np.arange(L - nrows, L)
-        q_pos = oracle.positions(rank, L)[rows]
-        pairs = 0
+    P = _cpu_share()
+    _ORACLE_POOL_STATE.update(host=host, cfg=cfg, rank=rank, backward=backward,
+                              k_pos=np.concatenate([oracle.positions(b, L) for b in blocks]))
+    tile = 256
+    tasks = [(h, r0, min(tile, L - r0)) for r0 in range(((L - 1) // tile) * tile, -1, -tile)
+             for h in range(cfg.heads)]
+    with mp.get_context("fork").Pool(P, initializer=_oracle_pool_init) as pool:
         t0 = time.perf_counter()
-        for h in heads:
-            kh = oracle.exact._kv_head(h, cfg.heads, cfg.n_kv_heads)
-            k = torch.cat([host.kv[b][0][:, kh:kh + 1] for b in blocks], dim=2)
-            v = torch.cat([host.kv[b][1][:, kh:kh + 1] for b in blocks], dim=2)
-            q = host.q[:, h:h + 1, rows]
-            do = host.dout[:, h:h + 1, rows]
-            oracle.attention_grads(q, k, v, do, q_pos, k_pos, cfg.causal)
-            pairs += int(sum(int((k_pos <= p).sum()) for p in q_pos)) * cfg.batch
-        return time.perf_counter() - t0, pairs
-
-    nrows = 256
-    dt, pairs = run([0], nrows)
-    heads = 1
-    if dt < target_s:
-        heads = int(min(cfg.heads, max(1, round(target_s / max(dt, 1e-3)))))
-        dt, pairs = run(list(range(heads)), nrows)
-    flops = (FWD_FLOPS_PER_PAIR_PER_D + BWD_FLOPS_PER_PAIR_PER_D) * cfg.head_dim * pairs
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "cpu_model": _cpu_model(),
-            "sample": (f"fp64 oracle forward + gradients for the last {nrows} query rows of "
-                       f"{heads} head(s) against all {len(k_pos)} keys ({pairs} unmasked pairs), "
-                       f"{dt:.1f} s"),
-            "seconds": round(dt, 2)}
+        pool.map(_oracle_task, tasks[:P], chunksize=1)
+        t_round = time.perf_counter() - t0
+        rounds = max(1, min(len(tasks) // P - 1, int(round(target_s / max(t_round, 1e-3)))))
+        todo = tasks[P:P + rounds * P] or tasks[:P]
+        t0 = time.perf_counter()
+        res = pool.map(_oracle_task, todo, chunksize=1)
+        wall = time.perf_counter() - t0
+    pairs = sum(r[0] for r in res)
+    per_pair = (FWD_FLOPS_PER_PAIR_PER_D + (BWD_FLOPS_PER_PAIR_PER_D if backward else 0))
+    flops = per_pair * cfg.head_dim * pairs
+    return {"value": flops / wall / 1e12, "unit": "TFLOP/s", "cores": P, "kind": "oracle",
+            "processes": P, "blas_threads_per_process": 1,
+            "host_cpus": os.cpu_count(), "cpu_model": _cpu_model(),
+            "sample": (f"fp64 oracle {'forward + gradients' if backward else 'forward'} of "
+                       f"{len(todo)} (head, 256-row tile) slices (the last tiles of each head "
+                       f"first) against all {len(_ORACLE_POOL_STATE['k_pos'])} keys, "
+                       f"{pairs} unmasked pairs, {wall:.1f} s on {P} processes"),
+            "seconds": round(wall, 2)}
 
 
 def _cpu_model():
+    """CPU model from lscpu, else /proc/cpuinfo."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
     try:
         with open("/proc/cpuinfo") as f:
             return next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
@@ -529,6 +591,20 @@ def _bench_ffn(args):
     print(json.dumps(result), flush=True)
 
 
+# Attention workloads that --config selects (the configs of the share's
+# parity tests): 3 (default) is the 16384-query causal share with its
+# backward; 2 and 5 are forward-only shares; 4 is the training share.
+SHARE_WORKLOADS = {
+    2: "non-causal share fwd: batch 2, 16 heads, head_dim 128, ring 8, 4096 local queries x 32768 keys",
+    3: "lwm7b-causal-ring-share fwd+bwd: batch 1, 32 heads, head_dim 128, ring 8, rank 7, "
+       "16384 local queries x 131072 keys",
+    4: "training share fwd+bwd: batch 1, 32 heads, head_dim 128, ring 4, rank 3, "
+       "8192 local queries x 32768 keys",
+    5: "million-token ring share fwd: batch 1, 32 heads, head_dim 128, ring 64, rank 31, "
+       "16384 local queries x 524288 keys (adversarial scores)",
+}
+
+
 def main():
     args = _parse()
     if args.trace_overlap:
@@ -550,22 +626,33 @@ def main():
     if args.ffn:
         _bench_ffn(args)
         return
+    if args.config not in SHARE_WORKLOADS:
+        print(f"--config {args.config}: choose one of {sorted(SHARE_WORKLOADS)}", file=sys.stderr)
+        sys.exit(2)
 
     import torch
 
-    from blockwise_ring_attention_amd import _lib, share
+    from blockwise_ring_attention_amd import share
     from blockwise_ring_attention_amd.configs import CONFIGS, scaled
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    _lib.load()
-    cfg = scaled(CONFIGS[3], backward=True, kv_heads=args.kv_heads)
+    backward = args.config in (3, 4)
+    cfg = scaled(CONFIGS[args.config], backward=backward, kv_heads=args.kv_heads)
     mha = cfg.n_kv_heads == cfg.heads
     rank = cfg.ranks[0]
     t_gen = time.perf_counter()
-    host = share.make_host_share(cfg, rank, seed=0, backward=True)
+    host = share.make_host_share(cfg, rank, seed=0, backward=backward)
+    t_gen = time.perf_counter() - t_gen
+    # The oracle's pool forks, so it runs before anything touches the GPU.
+    cpu = None if args.no_cpu_baseline else _cpu_baseline(host, cfg, rank, backward,
+                                                          args.cpu_seconds)
+
+    from blockwise_ring_attention_amd import _lib
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    _lib.load()
+    t_up = time.perf_counter()
     dev = share.upload(host)
     torch.cuda.synchronize()
-    t_gen = time.perf_counter() - t_gen
+    t_gen += time.perf_counter() - t_up
     main_stream = torch.cuda.current_stream()
     side = share.side_stream_for(dev.q.device)
 
@@ -578,7 +665,8 @@ def main():
 
     def step():
         fwd()
-        bwd()
+        if backward:
+            bwd()
 
     def timed(fn, steps, per_step=None):
         """Mean ms per step between two events around all steps (and, if
@@ -604,18 +692,18 @@ def main():
     ms_step, wall_step = timed(step, args.steps, step_ms)
     _lib.ring_attn_timing_enable(False)
     kernels = {}
-    for fam in ("fwd_bf16", "bwd_dq", "bwd_dkv"):
+    for fam in ("fwd_bf16", "bwd_dq", "bwd_dkv") if backward else ("fwd_bf16",):
         n, tot = _lib.ring_attn_timing_read(fam)
         kernels[fam] = {"launches": n, "total_ms": tot}
 
     pairs = cfg.pairs(rank)
     d = cfg.head_dim
     fwd_flops = FWD_FLOPS_PER_PAIR_PER_D * d * pairs
-    bwd_flops = BWD_FLOPS_PER_PAIR_PER_D * d * pairs
+    bwd_flops = BWD_FLOPS_PER_PAIR_PER_D * d * pairs if backward else 0
     tflops = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
 
     phases = {}
-    if not args.no_phases:
+    if backward and not args.no_phases:
         ms_fwd, _ = timed(fwd, args.steps)
         ms_bwd, _ = timed(bwd, args.steps)
         for name, ms, fl in (("fwd", ms_fwd, fwd_flops), ("bwd", ms_bwd, bwd_flops)):
@@ -624,6 +712,8 @@ def main():
                             "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
 
     # Roofline of the kernel family that takes the most time in the step.
+    # The committed counters were taken on the default workload only.
+    counters = mha and args.config == 3
     per_kernel = {}
     for fam, rec in kernels.items():
         if rec["launches"] == 0:
@@ -635,16 +725,18 @@ def main():
                            "total_ms_per_step": round(rec["total_ms"] / args.steps, 3),
                            "tflops": round(achieved, 1),
                            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                           "mfma_busy_pct_counter": _measured_mfma_util(fam) if mha else None}
+                           "mfma_busy_pct_counter": _measured_mfma_util(fam) if counters else None}
     dom = max(per_kernel, key=lambda f: per_kernel[f]["total_ms_per_step"])
     roofline = {"bound": "mfma", "achieved": per_kernel[dom]["tflops"], "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": per_kernel[dom]["frac"],
-                # the committed counters were taken on the multi-head workload
-                "traffic": _measured_traffic(dom) if mha else None,
+                "traffic": _measured_traffic(dom) if counters else None,
                 "traffic_unit": "HBM bytes per launch",
-                "mfma_busy_pct_counter": _measured_mfma_util(dom) if mha else None,
+                "mfma_busy_pct_counter": _measured_mfma_util(dom) if counters else None,
                 "kernel": dom}
 
+    workload = SHARE_WORKLOADS[args.config]
+    if cfg.n_kv_heads != cfg.heads:
+        workload += f", {cfg.n_kv_heads} shared key/value heads"
     result = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -658,14 +750,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": ("lwm7b-causal-ring-share fwd+bwd: batch 1, 32 heads, head_dim 128, "
-                                "ring 8, rank 7, 16384 local queries x 131072 keys"
-                                + (f", {cfg.n_kv_heads} shared key/value heads"
-                                   if cfg.n_kv_heads != cfg.heads else "")),
+        "config": {"workload": workload, "config": args.config,
+                   "pass": "fwd+bwd" if backward else "fwd",
                    "batch": cfg.batch, "heads": cfg.heads, "kv_heads": cfg.n_kv_heads,
                    "head_dim": d,
                    "ring_size": cfg.ring_size, "rank": rank, "local_queries": cfg.block_len,
-                   "keys": cfg.block_len * (rank + 1), "causal": cfg.causal,
+                   "keys": cfg.block_len * len(cfg.kv_blocks_seen(rank)), "causal": cfg.causal,
                    "q_chunk": cfg.q_chunk, "k_chunk": cfg.k_chunk,
                    "unmasked_pairs": pairs},
         "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
@@ -677,8 +767,8 @@ def main():
         "roofline": roofline,
         "input_setup_s": round(t_gen, 1),
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = _cpu_baseline(host, cfg, rank, args.cpu_seconds)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 
