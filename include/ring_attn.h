@@ -56,8 +56,15 @@
  *   ring_attn_init_acc.
  * - q_chunk / k_chunk are the query and key chunk sizes of the blockwise
  *   decomposition (sourcepulse project page, Highlighted Details: tuning
- *   knobs).  They must be >= 1.  They select the kernels' tile shapes and
- *   never change the result beyond rounding.
+ *   knobs).  They must be >= 1; they need not divide the lengths (ragged
+ *   last chunks are handled).  They select the kernels' tile shapes and never
+ *   change the result beyond rounding: for bf16 ring steps q_chunk >= 256
+ *   selects 256 query rows per workgroup (8 waves), otherwise 128 (4 waves);
+ *   k_chunk >= 64 selects 64-key tiles, otherwise 32.  Larger chunks (cfg
+ *   "512 / 1024") therefore run as 256 / 64: a chunk of 1024 keys of d = 128
+ *   in K and V is 512 KiB, more than the 160 KiB of LDS a compute unit has.
+ *   The backward always uses 256-row dQ tiles and 128-key dK/dV tiles; the
+ *   fp32 forward, one query row per thread.
  *
  * Errors: every entry point returns RA_OK (0) or a negative code, and never
  * throws.  Invalid arguments and unsupported shapes are detected on the host
@@ -134,7 +141,11 @@ int ring_attn_combine(float* o_a, float* lse_a, const float* o_b,
                       const float* lse_b, const ra_dims* dims, void* stream);
 
 /* Cast an fp32 [B, H, Lq, d] accumulator (o_acc or dq_acc) to out_dtype
- * (RA_BF16 with round-to-nearest-even, or RA_FP32 copy). */
+ * (RA_BF16 with round-to-nearest-even, or RA_FP32 copy).  The pages fix no
+ * output precision; the bf16 output with an fp32 running accumulator is the
+ * reading used (the accumulator stays fp32 across every ring step, so the
+ * blockwise fold adds no rounding of its own).  acc and out must not
+ * overlap (RA_ERR_INVALID). */
 int ring_attn_finalize(const float* acc, void* out, int out_dtype,
                        const ra_dims* dims, void* stream);
 
@@ -146,8 +157,12 @@ int ring_attn_bwd_prep(const float* o, const void* dout, float* delta,
                        const ra_dims* dims, void* stream);
 
 /* Backward ring step for block kb = (ring_rank - ring_step) mod ring_size.
- * Recomputes the probabilities from the saved final lse (natural log, as
- * left in lse_acc by the forward) and accumulates
+ * The pages do not discuss the backward; this is the exact gradient of
+ * sum(dO * O) for the forward above, computed blockwise with the
+ * probabilities recomputed per block rather than stored (the memory-efficient
+ * method keeps no attention matrix; Blockwise RingAttention keyword page,
+ * definition).  Recomputes the probabilities from the saved final lse
+ * (natural log, as left in lse_acc by the forward) and accumulates
  *     dq_acc += dQ  (this block's contribution to the member's dQ)
  *     dkv_io += [dK_kb, dV_kb]  (this member's contribution to block kb)
  * so a travelling dK/dV partial can collect every member's contribution.
