@@ -53,10 +53,13 @@ _SIGS = {
     "ring_attn_bwd_prep": ([_vp, _vp, _vp, ctypes.POINTER(Dims), _vp], _i),
     "ring_attn_bwd": ([_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp,
                        ctypes.POINTER(Dims), _vp], _i),
+    "ring_attn_bwd_workspace": ([ctypes.POINTER(Dims)], ctypes.c_int64),
+    "ring_attn_bwd_ws": ([_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp,
+                          ctypes.c_int64, ctypes.POINTER(Dims), _vp], _i),
     "ring_emu_fwd": ([_vp, ctypes.POINTER(_vp), _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp,
                       ctypes.POINTER(Dims), ctypes.POINTER(ctypes.c_int32), _i, _vp, _vp], _i),
     "ring_emu_bwd": ([_vp, ctypes.POINTER(_vp), _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(_vp),
-                      _vp, _vp, _i, _i, _i, _i, _i, _vp, ctypes.POINTER(Dims),
+                      _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, ctypes.c_int64, ctypes.POINTER(Dims),
                       ctypes.POINTER(ctypes.c_int32), _i, _vp, _vp], _i),
     "ring_attn_decode_chunk": ([ctypes.POINTER(Dims)], _i),
     "ring_attn_decode_splits": ([ctypes.POINTER(Dims), _i], _i),
@@ -299,6 +302,35 @@ def ring_attn_bwd(q, kv_block, dout, lse, delta, ring_rank, ring_step, ring_size
                                 _stream(stream)))
 
 
+def ring_attn_bwd_workspace(q, kv_block, scale=0.0) -> int:
+    """Bytes of workspace ring_attn_bwd_ws uses for these shapes (0: none)."""
+    dm = dims(q, kv_block.shape[3], scale, kv_block.shape[2])
+    n = load().ring_attn_bwd_workspace(ctypes.byref(dm))
+    _check(int(min(n, 0)))
+    return int(n)
+
+
+def ring_attn_bwd_ws(q, kv_block, dout, lse, delta, ring_rank, ring_step, ring_size, causal,
+                     q_chunk, k_chunk, dq_acc, dkv_io, work, scale=0.0, stream=None):
+    """ring_attn_bwd with a device workspace (a tensor, or None for none) that
+    lets the query heads sharing a key/value head run side by side."""
+    _need(kv_block, q.dtype, "kv_block")
+    _need(dout, q.dtype, "dout")
+    for t, n in ((lse, "lse"), (delta, "delta"), (dq_acc, "dq_acc"), (dkv_io, "dkv_io")):
+        _need(t, torch.float32, n)
+    nbytes = 0
+    if work is not None:
+        if not work.is_contiguous():
+            raise ValueError("work must be contiguous")
+        nbytes = work.numel() * work.element_size()
+    dm = dims(q, kv_block.shape[3], scale, kv_block.shape[2])
+    _check(load().ring_attn_bwd_ws(_ptr(q), _ptr(kv_block), _ptr(dout), _ptr(lse), _ptr(delta),
+                                   ring_rank, ring_step, ring_size, int(bool(causal)), q_chunk,
+                                   k_chunk, _ptr(dq_acc), _ptr(dkv_io),
+                                   _ptr(work) if work is not None else None, nbytes,
+                                   ctypes.byref(dm), _stream(stream)))
+
+
 def _ptr_array(ts: Sequence[Optional[torch.Tensor]]):
     arr = (_vp * len(ts))()
     for i, t in enumerate(ts):
@@ -333,7 +365,8 @@ def ring_emu_fwd(q, kv_pool, slots, ring_rank, ring_size, causal, q_chunk, k_chu
 
 def ring_emu_bwd(q, kv_pool, slots, dout, lse, delta, dkv_pool, dkv_slots, ring_rank, ring_size,
                  causal, q_chunk, k_chunk, dq_acc, scale=0.0, order=None, serialize=False,
-                 main_stream=None, side_stream=None):
+                 main_stream=None, side_stream=None, work=None):
+    """work: optional device workspace of ring_attn_bwd_workspace bytes."""
     if len(kv_pool) != ring_size or len(dkv_pool) != ring_size:
         raise ValueError("pools must have ring_size entries")
     ref = next(t for t in kv_pool if t is not None)
@@ -344,6 +377,8 @@ def ring_emu_bwd(q, kv_pool, slots, dout, lse, delta, dkv_pool, dkv_slots, ring_
                                _ptr(dout), _ptr(lse), _ptr(delta), _ptr_array(dkv_pool),
                                _ptr(dkv_slots[0]), _ptr(dkv_slots[1]), ring_rank, ring_size,
                                int(bool(causal)), q_chunk, k_chunk, _ptr(dq_acc),
+                               _ptr(work) if work is not None else None,
+                               work.numel() * work.element_size() if work is not None else 0,
                                ctypes.byref(dm), _order_array(order),
                                RA_EMU_SERIALIZE if serialize else RA_EMU_OVERLAP,
                                _vp(main.cuda_stream), _vp(side.cuda_stream)))

@@ -176,10 +176,40 @@ int ra_fwd_block(const void* q, const void* kv, int kb, int rank, int causal,
   return e == hipSuccess ? RA_OK : ra_hip_fail(e, "forward kernel launch");
 }
 
+int ra_bwd_dkv_splits(const ra_shape& s) {
+  const int G = s.Hkv > 0 ? s.H / s.Hkv : 1;
+  const int64_t wgs = (int64_t)s.B * s.Hkv * ((s.Lk + 127) / 128);  // 128 keys per workgroup
+  int S = 1;
+  while (S < G && wgs * S < 256) S *= 2;  // about one workgroup per compute unit
+  return S < G ? S : G;
+}
+
+int ra_bwd_ws_plan(const ra_shape& s, const void* work, int64_t work_bytes,
+                   const void* const* other, const size_t* othersz, int nother, int* nsplit) {
+  *nsplit = 1;
+  if (work_bytes < 0)
+    return ra_fail(RA_ERR_INVALID, "work_bytes %lld is negative", (long long)work_bytes);
+  if (work_bytes > 0 && !work) return ra_fail(RA_ERR_INVALID, "NULL workspace");
+  // As many dK/dV copies as the workspace holds, up to the preferred count.
+  const int64_t copyb = (int64_t)2 * s.kv_rows * s.D * 4;
+  if (copyb == 0) return RA_OK;
+  const int n = std::min<int64_t>(ra_bwd_dkv_splits(s), 1 + work_bytes / copyb);
+  if (n > 1) {
+    if ((uintptr_t)work % 16 != 0)
+      return ra_fail(RA_ERR_INVALID, "workspace must be 16-byte aligned");
+    const size_t wb = (size_t)(n - 1) * (size_t)copyb;
+    for (int i = 0; i < nother; ++i)
+      if (overlaps(work, wb, other[i], othersz[i]))
+        return ra_fail(RA_ERR_INVALID, "the workspace overlaps an input or an output");
+  }
+  *nsplit = n;
+  return RA_OK;
+}
+
 int ra_bwd_block(const void* q, const void* kv, const void* dout, const float* lse,
                  const float* delta, int kb, int rank, int causal, int q_chunk,
-                 int k_chunk, float* dq_acc, float* dkv, const ra_shape& s,
-                 hipStream_t stream) {
+                 int k_chunk, float* dq_acc, float* dkv, float* ws, int nsplit,
+                 const ra_shape& s, hipStream_t stream) {
   if (s.q_rows == 0 || s.Lk == 0) return RA_OK;
   if (causal && kb > rank) return RA_OK;
   ra_launch L{s.B, s.H, s.Lq, s.Lk, s.D, s.Hkv, s.scale, causal && kb == rank ? 1 : 0,
@@ -189,7 +219,7 @@ int ra_bwd_block(const void* q, const void* kv, const void* dout, const float* l
   tq.done();
   if (e != hipSuccess) return ra_hip_fail(e, "backward dQ kernel launch");
   Timed tkv(kBwdDkv, stream);
-  e = ra_launch_bwd_dkv(q, kv, dout, lse, delta, dkv, L);
+  e = ra_launch_bwd_dkv(q, kv, dout, lse, delta, dkv, ws, nsplit, L);
   tkv.done();
   return e == hipSuccess ? RA_OK : ra_hip_fail(e, "backward dK/dV kernel launch");
 }
@@ -340,7 +370,7 @@ int ra_decode_step(const void* q, const void* kv_block, int k_chunk, int S, floa
 
 extern "C" {
 
-int ring_attn_version(void) { return 203; }
+int ring_attn_version(void) { return 204; }
 
 int ring_attn_timing_enable(int on) {
   std::lock_guard<std::mutex> g(g_tmu);
@@ -470,7 +500,40 @@ int ring_attn_bwd(const void* q, const void* kv_block, const void* dout, const f
     return rc;
   const int kb = ra_block_of_step(ring_rank, ring_step, ring_size);
   return ra_bwd_block(q, kv_block, dout, lse, delta, kb, ring_rank, causal, q_chunk,
-                      k_chunk, dq_acc, dkv_io, s, (hipStream_t)stream);
+                      k_chunk, dq_acc, dkv_io, nullptr, 1, s, (hipStream_t)stream);
+}
+
+int64_t ring_attn_bwd_workspace(const ra_dims* dims) {
+  ra_shape s;
+  int rc = ra_check_dims(dims, &s);
+  if (rc) return rc;
+  return (int64_t)(ra_bwd_dkv_splits(s) - 1) * 2 * s.kv_rows * s.D * 4;
+}
+
+int ring_attn_bwd_ws(const void* q, const void* kv_block, const void* dout, const float* lse,
+                     const float* delta, int ring_rank, int ring_step, int ring_size,
+                     int causal, int q_chunk, int k_chunk, float* dq_acc, float* dkv_io,
+                     void* work, int64_t work_bytes, const ra_dims* dims, void* stream) {
+  ra_shape s;
+  int rc = ra_check_dims(dims, &s);
+  if (rc) return rc;
+  if (s.dtype != RA_BF16)
+    return ra_fail(RA_ERR_UNSUPPORTED, "backward is implemented for bf16 inputs only");
+  if ((rc = ra_check_ring(ring_rank, ring_step, ring_size, causal, q_chunk, k_chunk, s)))
+    return rc;
+  if ((rc = ra_check_bwd_buffers(q, kv_block, dout, lse, delta, dq_acc, dkv_io, s)))
+    return rc;
+  const size_t qb = (size_t)s.q_rows * s.D * s.elem;
+  const size_t kvb = (size_t)2 * s.kv_rows * s.D * s.elem;
+  const size_t lb = (size_t)s.q_rows * 4, dqb = (size_t)s.q_rows * s.D * 4;
+  const size_t dkvb = (size_t)2 * s.kv_rows * s.D * 4;
+  const void* other[7] = {q, kv_block, dout, lse, delta, dq_acc, dkv_io};
+  const size_t othersz[7] = {qb, kvb, qb, lb, lb, dqb, dkvb};
+  int nsplit = 1;
+  if ((rc = ra_bwd_ws_plan(s, work, work_bytes, other, othersz, 7, &nsplit))) return rc;
+  const int kb = ra_block_of_step(ring_rank, ring_step, ring_size);
+  return ra_bwd_block(q, kv_block, dout, lse, delta, kb, ring_rank, causal, q_chunk,
+                      k_chunk, dq_acc, dkv_io, (float*)work, nsplit, s, (hipStream_t)stream);
 }
 
 int ring_attn_decode_chunk(const ra_dims* dims) {

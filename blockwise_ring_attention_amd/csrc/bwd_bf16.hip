@@ -276,8 +276,8 @@ template <int D, int BQ, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ KV,
     const bf16* __restrict__ dO, const float* __restrict__ LSE,
-    const float* __restrict__ Delta, float* __restrict__ dKV, int BH, int H, int G, int qj, int Lq,
-    int Lk, int n_kt, int diag, float c2, float scale) {
+    const float* __restrict__ Delta, float* __restrict__ dKV, float* __restrict__ WS, int BH, int H,
+    int G, int qj, int ws_store, int Lq, int Lk, int n_kt, int diag, float c2, float scale) {
   using C = TileCfg<D, BQ, NW>;
   constexpr int BK = NW * 32;  // keys per workgroup
   constexpr int DS = D / 16, DD = D / 32;
@@ -292,10 +292,16 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: loop bounds derive from it
   const int l32 = lane & 31, hl = lane >> 5;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  // This workgroup's key/value head, and the query head of its group that
-  // this launch handles (one launch per member qj of a group of G).
-  const int kvbh = tile / n_kt;
-  const int bh = (kvbh / (H / G)) * H + (kvbh % (H / G)) * G + qj;
+  // This workgroup's split sp, key/value head and key tile.  A launch handles
+  // query heads qj .. qj + nsplit - 1 of every group, split sp taking member
+  // qj + sp; split 0 adds into dKV, split sp > 0 into its own copy of dKV in
+  // WS (stored rather than added when ws_store is set).  Consecutive
+  // workgroups (one XCD) share the split and head, so they stream the same
+  // query rows.
+  const int per_split = (BH / G) * n_kt;
+  const int sp = tile / per_split;
+  const int kvbh = (tile % per_split) / n_kt;
+  const int bh = (kvbh / (H / G)) * H + (kvbh % (H / G)) * G + qj + sp;
   const int k0 = (tile % n_kt) * BK;  // small k0 first: the most causal work
   const int kw0 = k0 + wave * 32;
   const int kj = kw0 + l32;
@@ -636,8 +642,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
 
   // dK / dV rows: lane holds head-dim column dd*32 + l32 of keys
   // kw0 + 8*(r/4) + 4*hl + r%4.
-  float* dKp = dKV + (size_t)kvbh * Lk * D;
-  float* dVp = dKV + ((size_t)(BH / G) + kvbh) * Lk * D;
+  float* out = sp == 0 ? dKV : WS + (size_t)(sp - 1) * 2 * (BH / G) * Lk * D;
+  const bool add = sp == 0 || !ws_store;
+  float* dKp = out + (size_t)kvbh * Lk * D;
+  float* dVp = out + ((size_t)(BH / G) + kvbh) * Lk * D;
 #pragma unroll
   for (int dd = 0; dd < DD; ++dd) {
     // all loads of this head-dim tile first, then the stores
@@ -646,8 +654,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
     for (int r = 0; r < 16; ++r) {
       const int key = kw0 + 8 * (r >> 2) + 4 * hl + (r & 3);
       const size_t o = (size_t)min(key, Lk - 1) * D + dd * 32 + l32;
-      ok[r] = dKp[o];
-      ov[r] = dVp[o];
+      ok[r] = add ? dKp[o] : 0.f;
+      ov[r] = add ? dVp[o] : 0.f;
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -665,9 +673,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
 
 // BN = 64 keys per dQ tile with eight waves (256 query rows per workgroup);
 // BQ = 64 queries per dK/dV tile with four waves (128 keys per workgroup).
-// With G query heads per key/value head, the dK/dV kernel runs once per
-// member of a group, each launch adding that query head's contribution
-// (deterministic, in a fixed order).
+// With G query heads per key/value head, the dK/dV kernel runs over the
+// members of a group in launches of nsplit members each (the last one may
+// hold fewer); split 0 adds into dkv, split s > 0 into copy s - 1 of dkv in
+// ws, which the first launch stores and the later ones add to, and a last
+// pass adds the copies into dkv in copy order.  Every sum is taken in a
+// fixed order, so results are deterministic.
 hipError_t ra_launch_bwd_dq(const void* q, const void* kv, const void* dout,
                             const float* lse, const float* delta, float* dq_acc,
                             const ra_launch& a) {
@@ -688,24 +699,29 @@ hipError_t ra_launch_bwd_dq(const void* q, const void* kv, const void* dout,
 }
 
 hipError_t ra_launch_bwd_dkv(const void* q, const void* kv, const void* dout,
-                             const float* lse, const float* delta, float* dkv,
-                             const ra_launch& a) {
+                             const float* lse, const float* delta, float* dkv, float* ws,
+                             int nsplit, const ra_launch& a) {
   constexpr int NW = 4, BK = NW * 32;
   const int BH = a.B * a.H, G = a.H / a.Hkv, BHkv = a.B * a.Hkv;
   const int n_kt = (a.Lk + BK - 1) / BK;
   if ((long long)n_kt * BHkv <= 0) return hipSuccess;
+  if (nsplit < 1 || nsplit > G || (nsplit > 1 && !ws)) return hipErrorInvalidValue;
   const float c2 = a.scale * kLog2e;
   if (a.D != 128 && a.D != 64) return hipErrorInvalidValue;
-  for (int qj = 0; qj < G; ++qj) {
-#define RA_DKV(DD)                                                                            \
-  hipLaunchKernelGGL((dkv_kernel<DD, 64, NW>), dim3(n_kt * BHkv), dim3(NW * 64), 0, a.stream, \
-                     (const bf16*)q, (const bf16*)kv, (const bf16*)dout, lse, delta, dkv, BH,   \
-                     a.H, G, qj, a.Lq, a.Lk, n_kt, a.diag, c2, a.scale)
+  for (int qj = 0; qj < G; qj += nsplit) {
+    const int ns = min(nsplit, G - qj);
+    const unsigned grid = (unsigned)(n_kt * BHkv * ns);
+#define RA_DKV(DD)                                                                             \
+  hipLaunchKernelGGL((dkv_kernel<DD, 64, NW>), dim3(grid), dim3(NW * 64), 0, a.stream,          \
+                     (const bf16*)q, (const bf16*)kv, (const bf16*)dout, lse, delta, dkv, ws,   \
+                     BH, a.H, G, qj, qj == 0 ? 1 : 0, a.Lq, a.Lk, n_kt, a.diag, c2, a.scale)
     if (a.D == 128) RA_DKV(128);
     else RA_DKV(64);
 #undef RA_DKV
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (nsplit > 1)
+    return ra_launch_add_copies(dkv, ws, nsplit - 1, (int64_t)2 * BHkv * a.Lk * a.D, a.stream);
   return hipSuccess;
 }

@@ -97,7 +97,29 @@ __global__ void bwd_prep_kernel(const float* __restrict__ o, const T* __restrict
   if (row < rows && sub == 0) delta[row] = acc;
 }
 
+// acc <- acc + c_0 + c_1 + ... in copy order (n4 float4 per copy): the
+// dK/dV copies of the query heads that ran side by side.
+__global__ void add_copies_kernel(f32x4* __restrict__ acc, const f32x4* __restrict__ copies,
+                                  int ncopies, int64_t n4) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    f32x4 v = acc[i];
+    for (int c = 0; c < ncopies; ++c) v += copies[c * n4 + i];
+    acc[i] = v;
+  }
+}
+
 }  // namespace
+
+hipError_t ra_launch_add_copies(float* acc, const float* copies, int ncopies, int64_t n,
+                                hipStream_t s) {
+  const int64_t n4 = n / 4;  // head_dim is a multiple of 4
+  unsigned grid = blocks_for(n4, kThreads);
+  if (grid > 65536) grid = 65536;
+  hipLaunchKernelGGL(add_copies_kernel, dim3(grid), dim3(kThreads), 0, s, (f32x4*)acc,
+                     (const f32x4*)copies, ncopies, n4);
+  return hipGetLastError();
+}
 
 hipError_t ra_launch_init_acc(float* o_acc, float* lse_acc, int64_t rows, int D,
                               hipStream_t s) {

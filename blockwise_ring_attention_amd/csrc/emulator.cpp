@@ -163,9 +163,9 @@ extern "C" int ring_emu_bwd(const void* q, const void* const* kv_pool, void* slo
                             void* slot1, const void* dout, const float* lse,
                             const float* delta, float* const* dkv_pool, float* dkv_slot0,
                             float* dkv_slot1, int ring_rank, int ring_size, int causal,
-                            int q_chunk, int k_chunk, float* dq_acc, const ra_dims* dims,
-                            const int32_t* order, int mode, void* main_stream,
-                            void* side_stream) {
+                            int q_chunk, int k_chunk, float* dq_acc, void* work,
+                            int64_t work_bytes, const ra_dims* dims, const int32_t* order,
+                            int mode, void* main_stream, void* side_stream) {
   ra_shape s;
   int rc = ra_check_dims(dims, &s);
   if (rc) return rc;
@@ -182,6 +182,7 @@ extern "C" int ring_emu_bwd(const void* q, const void* const* kv_pool, void* slo
   const size_t dkv_bytes = (size_t)2 * s.kv_rows * s.D * 4;
   void* slots[2] = {slot0, slot1};
   float* dslots[2] = {dkv_slot0, dkv_slot1};
+  int nsplit = 1;
   std::vector<int> copy_block;
   for (int kb : blocks) {
     if (!kv_pool[kb] || !dkv_pool[kb])
@@ -196,6 +197,28 @@ extern "C" int ring_emu_bwd(const void* q, const void* const* kv_pool, void* slo
   for (int i = 0; i < 2 && i < nc; ++i)
     if ((rc = ra_check_bwd_buffers(q, slots[i], dout, lse, delta, dq_acc, dslots[i], s)))
       return rc;
+  // The workspace must stay clear of every buffer of the share.
+  {
+    const size_t qb = (size_t)s.q_rows * s.D * s.elem, lb = (size_t)s.q_rows * 4;
+    const size_t dqb = (size_t)s.q_rows * s.D * 4;
+    std::vector<const void*> other = {q, dout, lse, delta, dq_acc};
+    std::vector<size_t> othersz = {qb, qb, lb, lb, dqb};
+    for (int kb : blocks) {
+      other.push_back(kv_pool[kb]);
+      othersz.push_back(kv_bytes);
+      other.push_back(dkv_pool[kb]);
+      othersz.push_back(dkv_bytes);
+    }
+    for (int i = 0; i < 2 && i < nc; ++i) {
+      other.push_back(slots[i]);
+      othersz.push_back(kv_bytes);
+      other.push_back(dslots[i]);
+      othersz.push_back(dkv_bytes);
+    }
+    if ((rc = ra_bwd_ws_plan(s, work, work_bytes, other.data(), othersz.data(),
+                             (int)other.size(), &nsplit)))
+      return rc;
+  }
 
   hipStream_t main = (hipStream_t)main_stream;
   hipStream_t side = mode == RA_EMU_SERIALIZE ? main : (hipStream_t)side_stream;
@@ -253,7 +276,7 @@ extern "C" int ring_emu_bwd(const void* q, const void* const* kv_pool, void* slo
       dsrc = dslots[slot];
     }
     if ((rc = ra_bwd_block(q, src, dout, lse, delta, kb, ring_rank, causal, q_chunk, k_chunk,
-                           dq_acc, dsrc, s, main)))
+                           dq_acc, dsrc, (float*)work, nsplit, s, main)))
       return rc;
     if (slot >= 0) {
       if (mode == RA_EMU_OVERLAP) RA_HIP(hipEventRecord(ev.e[2 + slot], main), "hipEventRecord");

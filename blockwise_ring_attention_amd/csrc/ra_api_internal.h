@@ -31,7 +31,15 @@ int ra_check_bwd_buffers(const void* q, const void* kv, const void* dout,
 int ra_fwd_block(const void* q, const void* kv, int kb, int rank, int causal,
                  int q_chunk, int k_chunk, float* o_acc, float* lse_acc,
                  const ra_shape& s, hipStream_t stream);
+// ws: (nsplit - 1) fp32 copies of dkv, or nullptr with nsplit == 1.
 int ra_bwd_block(const void* q, const void* kv, const void* dout, const float* lse,
                  const float* delta, int kb, int rank, int causal, int q_chunk,
-                 int k_chunk, float* dq_acc, float* dkv, const ra_shape& s,
-                 hipStream_t stream);
+                 int k_chunk, float* dq_acc, float* dkv, float* ws, int nsplit,
+                 const ra_shape& s, hipStream_t stream);
+// Query heads of a group whose dK/dV run side by side, for about one
+// workgroup per compute unit (1 when every head has its own key/value head).
+int ra_bwd_dkv_splits(const ra_shape& s);
+// Copies a backward call can use from a workspace of work_bytes (validated:
+// sign, NULL, 16-byte alignment, no overlap with the nother given buffers).
+int ra_bwd_ws_plan(const ra_shape& s, const void* work, int64_t work_bytes,
+                   const void* const* other, const size_t* othersz, int nother, int* nsplit);

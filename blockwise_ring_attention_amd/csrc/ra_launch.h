@@ -65,6 +65,11 @@ hipError_t ra_launch_bwd_prep(const float* o, const void* dout, int dtype,
 hipError_t ra_launch_bwd_dq(const void* q, const void* kv, const void* dout,
                             const float* lse, const float* delta, float* dq_acc,
                             const ra_launch& a);
+// dK/dV over the G query heads of each key/value head, nsplit heads side by
+// side per launch; nsplit > 1 needs ws, (nsplit - 1) fp32 copies of dkv.
 hipError_t ra_launch_bwd_dkv(const void* q, const void* kv, const void* dout,
-                             const float* lse, const float* delta, float* dkv,
-                             const ra_launch& a);
+                             const float* lse, const float* delta, float* dkv, float* ws,
+                             int nsplit, const ra_launch& a);
+// acc[i] += copies[0][i] + copies[1][i] + ... (in copy order), n floats per copy.
+hipError_t ra_launch_add_copies(float* acc, const float* copies, int ncopies, int64_t n,
+                                hipStream_t s);

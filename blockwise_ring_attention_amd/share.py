@@ -55,6 +55,7 @@ class DeviceShare:
     dq_acc: Optional[torch.Tensor] = None
     dkv_pool: List[Optional[torch.Tensor]] = field(default_factory=list)
     dkv_slots: List[torch.Tensor] = field(default_factory=list)
+    work: Optional[torch.Tensor] = None  # dK/dV workspace for shared key/value heads
 
 
 def upload(host: HostShare, device: str = "cuda") -> DeviceShare:
@@ -78,6 +79,9 @@ def upload(host: HostShare, device: str = "cuda") -> DeviceShare:
                                                            device=device) for t in pool]
         dev.dkv_slots = [torch.empty(ref.shape, dtype=torch.float32, device=device)
                          for _ in range(2)]
+        nbytes = _lib.ring_attn_bwd_workspace(q, ref)
+        if nbytes > 0:
+            dev.work = torch.empty(nbytes, dtype=torch.uint8, device=device)
     return dev
 
 
@@ -106,9 +110,12 @@ def forward(dev: DeviceShare, q_chunk: Optional[int] = None, k_chunk: Optional[i
 
 
 def backward(dev: DeviceShare, q_chunk: Optional[int] = None, k_chunk: Optional[int] = None,
-             order=None, serialize: bool = False, side_stream=None) -> None:
+             order=None, serialize: bool = False, side_stream=None,
+             use_work: bool = True) -> None:
     """Gradients of the finished forward share: dq_acc, and dkv_pool[kb] +=
-    this member's dK/dV contribution for every block it sees."""
+    this member's dK/dV contribution for every block it sees.  With shared
+    key/value heads the share's workspace (if any) lets query heads of a
+    group run side by side (use_work=False: one after another)."""
     cfg = dev.cfg
     if side_stream is None and not serialize:
         side_stream = side_stream_for(dev.q.device)
@@ -117,7 +124,8 @@ def backward(dev: DeviceShare, q_chunk: Optional[int] = None, k_chunk: Optional[
     _lib.ring_emu_bwd(dev.q, dev.pool, dev.slots, dev.dout, dev.lse_acc, dev.delta,
                       dev.dkv_pool, dev.dkv_slots, dev.rank, cfg.ring_size, cfg.causal,
                       q_chunk or cfg.q_chunk, k_chunk or cfg.k_chunk, dev.dq_acc,
-                      order=order, serialize=serialize, side_stream=side_stream)
+                      order=order, serialize=serialize, side_stream=side_stream,
+                      work=dev.work if use_work else None)
 
 
 def finalize(dev: DeviceShare) -> torch.Tensor:

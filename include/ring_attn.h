@@ -21,7 +21,7 @@
  *   caller's next synchronisation.
  * - Every compute entry point (ring_attn_init_acc, ring_attn_fwd,
  *   ring_attn_fwd_decode, ring_attn_fwd_decode_noalloc, ring_attn_combine,
- *   ring_attn_finalize, ring_attn_bwd_prep, ring_attn_bwd, ring_ffn_fwd,
+ *   ring_attn_finalize, ring_attn_bwd_prep, ring_attn_bwd, ring_attn_bwd_ws, ring_ffn_fwd,
  *   ring_ffn_bwd) only
  *   launches kernels on the given stream: no allocation, no hipMemset, no
  *   synchronisation, so a sequence of them may be captured into a HIP graph
@@ -177,6 +177,34 @@ int ring_attn_bwd(const void* q, const void* kv_block, const void* dout,
                   int k_chunk, float* dq_acc, float* dkv_io,
                   const ra_dims* dims, void* stream);
 
+/* The same backward step with a caller-provided workspace, for shared
+ * key/value heads.  The dK/dV of a key/value head sums the contributions of
+ * the G = H / Hkv query heads of its group (definition above); ring_attn_bwd
+ * takes them one query head after another over the head's key tiles of 128
+ * keys, so with few key/value heads (MQA: B * Hkv * ceil(Lk / 128)
+ * workgroups) part of the chip idles.  ring_attn_bwd_ws runs S query heads of
+ * each group side by side: the first adds into dkv_io as before, each other
+ * one into a private fp32 copy of dkv_io in `work` ([S-1][2, B, Hkv, Lk, d]),
+ * and the copies are added into dkv_io at the end of the call, in copy
+ * order.  Every sum is taken in a fixed order, so the result is
+ * deterministic for a given S; it differs from ring_attn_bwd only by the
+ * order of fp32 additions.
+ *   ring_attn_bwd_workspace(dims) returns the bytes of `work` for the
+ *   preferred S (about one workgroup per compute unit, at most G; 0 when
+ *   S = 1, e.g. Hkv == H), or a negative error code.
+ *   ring_attn_bwd_ws uses as many copies as work_bytes holds, up to that
+ *   preferred count (work_bytes == 0 is ring_attn_bwd).  work must be
+ *   16-byte aligned and must not overlap any other argument; its contents on
+ *   return are unspecified; work_bytes < 0, or work == NULL with
+ *   work_bytes > 0, is RA_ERR_INVALID.  All other arguments and errors as
+ *   ring_attn_bwd. */
+int64_t ring_attn_bwd_workspace(const ra_dims* dims);
+int ring_attn_bwd_ws(const void* q, const void* kv_block, const void* dout,
+                     const float* lse, const float* delta, int ring_rank,
+                     int ring_step, int ring_size, int causal, int q_chunk,
+                     int k_chunk, float* dq_acc, float* dkv_io, void* work,
+                     int64_t work_bytes, const ra_dims* dims, void* stream);
+
 /* ---- decode-shaped step ---------------------------------------------------
  * The inference use of the method (Ring Attention with Blockwise
  * Transformers, abstract: training and inference of long sequences): a few
@@ -317,14 +345,16 @@ int ring_emu_fwd(const void* q, const void* const* kv_pool, void* slot0,
  * member), so on return dkv_pool[kb] += this member's dK/dV for every block
  * it sees, in ring order.  dq_acc += the member's dQ.  dkv_slot0/1 are two
  * fp32 device buffers of one dK/dV block each.  lse and delta are those of
- * the finished forward share (ring_attn_bwd_prep). */
+ * the finished forward share (ring_attn_bwd_prep).  work / work_bytes: the
+ * optional dK/dV workspace of ring_attn_bwd_ws (NULL / 0 for none), reused
+ * by every block; it must not overlap any other buffer of the share. */
 int ring_emu_bwd(const void* q, const void* const* kv_pool, void* slot0,
                  void* slot1, const void* dout, const float* lse,
                  const float* delta, float* const* dkv_pool, float* dkv_slot0,
                  float* dkv_slot1, int ring_rank, int ring_size, int causal,
-                 int q_chunk, int k_chunk, float* dq_acc, const ra_dims* dims,
-                 const int32_t* order, int mode, void* main_stream,
-                 void* side_stream);
+                 int q_chunk, int k_chunk, float* dq_acc, void* work,
+                 int64_t work_bytes, const ra_dims* dims, const int32_t* order,
+                 int mode, void* main_stream, void* side_stream);
 
 /* ---- kernel timing (diagnostics) ---------------------------------------
  * While enabled, each attention kernel the library launches is bracketed by

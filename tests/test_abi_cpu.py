@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
               "ring_attn_finalize", "ring_attn_init_acc", "ring_attn_last_error",
               "ring_attn_version", "ring_emu_fwd", "ring_emu_bwd", "ring_attn_fwd_decode",
               "ring_attn_decode_chunk", "ring_attn_decode_splits", "ring_ffn_fwd",
-              "ring_attn_fwd_decode_noalloc",
+              "ring_attn_fwd_decode_noalloc", "ring_attn_bwd_ws", "ring_attn_bwd_workspace",
               "ring_ffn_bwd", "ring_ffn_bwd_workspace"):
         assert n in names
     assert sorted(_lib.EXPORTS) == names, "binding and header disagree"
@@ -41,7 +41,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.ring_attn_version() == 203
+    assert lib.ring_attn_version() == 204
     assert lib.ring_attn_last_error() == b""
 
 
@@ -94,6 +94,55 @@ def test_unsupported_and_invalid_dims(lib):
     assert lib.ring_attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, 1, 1, 64, 64, FAKE, FAKE,
                              ctypes.byref(d), None) == -2
     assert b"bf16" in lib.ring_attn_last_error()
+
+
+def _bwd_ws(lib, dims, work, nbytes, **kw):
+    p = dict(q=1 << 40, kv=2 << 40, do=3 << 40, lse=4 << 40, delta=5 << 40, dq=6 << 40,
+             dkv=7 << 40)
+    p.update(kw)
+    v = {k: ctypes.c_void_p(x) if x is not None else None for k, x in p.items()}
+    return lib.ring_attn_bwd_ws(v["q"], v["kv"], v["do"], v["lse"], v["delta"], 0, 0, 1, 1,
+                                256, 64, v["dq"], v["dkv"],
+                                ctypes.c_void_p(work) if work is not None else None, nbytes,
+                                ctypes.byref(dims) if dims is not None else None, None)
+
+
+def test_bwd_workspace_planning(lib):
+    """Shared key/value heads run enough query heads side by side for about
+    one workgroup (128 keys) per compute unit, never more than the group."""
+    def ws(**kw):
+        return lib.ring_attn_bwd_workspace(ctypes.byref(_dims(**kw)))
+    copy = lambda b, hkv, lk, d: 2 * b * hkv * lk * d * 4
+    assert ws(heads=32, q_len=16384, kv_len=16384) == 0                 # one kv head each
+    assert ws(heads=32, kv_heads=8, q_len=16384, kv_len=16384) == 0     # 1024 workgroups
+    # MQA: 128 workgroups, two heads side by side, one copy
+    assert ws(heads=32, kv_heads=1, q_len=16384, kv_len=16384) == copy(1, 1, 16384, 128)
+    # 16 workgroups -> 16 side by side, capped at the group of 8
+    assert ws(heads=8, kv_heads=1, q_len=2048, kv_len=2048) == 7 * copy(1, 1, 2048, 128)
+    assert ws(heads=32, kv_heads=2, q_len=4096, kv_len=4096, head_dim=64) == \
+        3 * copy(1, 2, 4096, 64)                                          # 64 wgs -> 4 side by side
+    assert lib.ring_attn_bwd_workspace(None) == -1
+    assert lib.ring_attn_bwd_workspace(ctypes.byref(_dims(head_dim=96))) == -2
+
+
+def test_bwd_ws_rejects_invalid(lib):
+    mqa = _dims(heads=32, kv_heads=1, q_len=16384, kv_len=16384)
+    need = lib.ring_attn_bwd_workspace(ctypes.byref(mqa))
+    far = 8 << 40
+    assert _bwd_ws(lib, None, far, need) == -1
+    assert _bwd_ws(lib, mqa, far, -1) == -1
+    assert _bwd_ws(lib, mqa, None, need) == -1
+    assert b"NULL workspace" in lib.ring_attn_last_error()
+    assert _bwd_ws(lib, mqa, far + 4, need) == -1
+    assert b"aligned" in lib.ring_attn_last_error()
+    assert _bwd_ws(lib, mqa, (7 << 40) + 4096, need) == -1             # overlaps dkv_io
+    assert b"workspace overlaps" in lib.ring_attn_last_error()
+    assert _bwd_ws(lib, mqa, 1 << 40, need) == -1                      # overlaps q
+    assert _bwd_ws(lib, _dims(dtype=1), far, need) == -2
+    assert _bwd_ws(lib, mqa, far, need, q=None) == -1
+    # nothing to compute: no pointer is touched
+    nul = dict(q=None, kv=None, do=None, lse=None, delta=None, dq=None, dkv=None)
+    assert _bwd_ws(lib, _dims(heads=32, kv_heads=1, q_len=0, kv_len=0), None, 0, **nul) == 0
 
 
 def test_empty_problems_are_no_ops(lib):

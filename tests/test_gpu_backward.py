@@ -162,16 +162,23 @@ def test_causal_independence_bitwise():
     assert torch.equal(a.dq_acc[:, :, :p + 1], b.dq_acc[:, :, :p + 1])
 
 
+@pytest.mark.parametrize("use_work", [True, False], ids=["side-by-side", "one-by-one"])
 @pytest.mark.parametrize("kv_heads", [1, 2])
-def test_shared_kv_heads_backward(kv_heads):
+def test_shared_kv_heads_backward(kv_heads, use_work):
     """MQA (one key/value head) and GQA (two, for four query heads): dK/dV of
-    a shared head sums its query heads' contributions (one launch per group
-    member), element by element against the oracle."""
+    a shared head sums its query heads' contributions, element by element
+    against the oracle, with the group's query heads side by side (dK/dV
+    copies in the workspace: 4 for MQA, 2 for GQA here) or one launch per
+    member."""
     cfg = ShareConfig(98, f"shared-kv{kv_heads}", "bf16", 1, 4, 128, 3, 200, (2,), True,
                       256, 64, backward=True, kv_heads=kv_heads)
     host = share.make_host_share(cfg, 2, seed=8, backward=True)
     assert host.kv[0].shape[2] == kv_heads
-    dev = _run(host)
+    dev = share.upload(host)
+    assert (dev.work is not None) and dev.work.numel() == (4 // kv_heads - 1) * 2 * kv_heads * 200 * 128 * 4
+    share.forward(dev)
+    share.backward(dev, use_work=use_work)
+    torch.cuda.synchronize()
     dq_ref, per_block = _oracle_grads(host)
     check("dq", dev.dq_acc, dq_ref, "bf16")
     for b, (dk_ref, dv_ref) in per_block.items():
@@ -203,6 +210,61 @@ def test_shared_kv_heads_full_size():
         check(f"dk[{kb}] kvh{kh}", dev.dkv_pool[kb][0][:, [kh]], dk_ref, "bf16")
         check(f"dv[{kb}] kvh{kh}", dev.dkv_pool[kb][1][:, [kh]], dv_ref, "bf16")
     assert torch.isfinite(dev.dq_acc).all()
+
+
+def test_mqa_full_size_side_by_side():
+    """MQA share, 32 query heads on one key/value head (rank 3 of 4, 2048
+    tokens per member): 16 query heads run side by side in two launches (15
+    workspace copies stored by the first, added to by the second); dK/dV of
+    every block and dQ of every head in full, against the oracle."""
+    cfg = ShareConfig(99, "mqa-train", "bf16", 1, 32, 128, 4, 2048, (3,), True, 256, 64,
+                      backward=True, kv_heads=1)
+    host = share.make_host_share(cfg, 3, seed=5, backward=True)
+    dev = share.upload(host)
+    assert dev.work.numel() == 15 * 2 * 2048 * 128 * 4
+    print("mqa: running forward + backward share", flush=True)
+    share.forward(dev)
+    share.backward(dev)
+    torch.cuda.synchronize()
+    print("mqa: oracle gradients of the whole share", flush=True)
+    dq_ref, per_block = _oracle_grads(host)
+    check("dq", dev.dq_acc, dq_ref, "bf16")
+    for kb, (dk_ref, dv_ref) in per_block.items():
+        check(f"dk[{kb}]", dev.dkv_pool[kb][0], dk_ref, "bf16")
+        check(f"dv[{kb}]", dev.dkv_pool[kb][1], dv_ref, "bf16")
+
+
+def test_mqa_benchmark_shape_side_by_side_matches_one_by_one():
+    """The MQA training share at the benchmark's size (rank 7 of 8, 16384
+    tokens per member, 32 query heads on one key/value head): two query
+    heads side by side give dK/dV that differ from one head after another
+    only by the order of fp32 additions, and are bitwise repeatable.  (Each
+    dK/dV element sums all 32 heads' rows over 131072 keys: past what the
+    oracle can take at this size; the sequential path is pinned to the
+    oracle at full size for GQA.)"""
+    cfg = ShareConfig(99, "mqa-bench", "bf16", 1, 32, 128, 8, 16384, (7,), True, 256, 64,
+                      backward=True, kv_heads=1)
+    host = share.make_host_share(cfg, 7, seed=0, backward=True)
+    dev = share.upload(host)
+    assert dev.work.numel() == 2 * 16384 * 128 * 4                      # one copy
+    share.forward(dev)
+    out = []
+    for use_work in (True, True, False):
+        print(f"mqa bench shape: backward use_work={use_work}", flush=True)
+        for t in dev.dkv_pool:
+            if t is not None:
+                t.zero_()
+        share.backward(dev, use_work=use_work)
+        torch.cuda.synchronize()
+        out.append(([t.clone() for t in dev.dkv_pool if t is not None], dev.dq_acc.clone()))
+    (a, dqa), (b, dqb), (c, dqc) = out
+    assert torch.equal(dqa, dqb) and torch.equal(dqa, dqc)
+    for x, y, z in zip(a, b, c):
+        assert torch.equal(x, y)
+        assert torch.isfinite(x).all()
+        rel = (torch.linalg.vector_norm(x - z) / torch.linalg.vector_norm(z)).item()
+        assert rel < 1e-5, rel
+        assert (x - z).abs().max().item() <= 1e-4 * z.abs().max().item()
 
 
 def test_benchmark_training_share_full_size():
