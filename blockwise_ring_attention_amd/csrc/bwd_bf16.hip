@@ -51,11 +51,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
   using C = TileCfg<D, BN, NW>;
   constexpr int BM = NW * 32;
   constexpr int KK = BN / 32, DS = D / 16, DD = D / 32;
-  // K ring: iteration t reads K tiles t-1 .. t+1, has t+2 in flight and
-  // issues t+3.  V ring: reads t, t+1, t+2 in flight, issues t+3.
-  constexpr int NK = 5, NV = 4;
-  constexpr int VBASE = NK * C::TILEB;
-  __shared__ __attribute__((aligned(1024))) char smem[(NK + NV) * C::TILEB];
+  // Ring of NR slots, each a K tile followed by its V tile.  Iteration t
+  // reads K tiles t-1 .. t+1 and V tiles t, t+1, has tiles t+2 in flight and
+  // issues t+3.  A V tile sits a fixed TILEB after its K tile, so both
+  // are addressed from one register plus an immediate offset.
+  constexpr int NR = 5;
+  __shared__ __attribute__((aligned(1024))) char smem[NR * 2 * C::TILEB];
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lvoid*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -87,10 +88,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
   using Loader = TileLoader<D, BN, NW, false>;
   const Loader loader(wave, lane);
   auto issue_k = [&](int t) __attribute__((always_inline)) {
-    loader.issue(smem_lds + (t % NK) * C::TILEB, Kp, t * BN, Lk);
+    loader.issue(smem_lds + (t % NR) * 2 * C::TILEB, Kp, t * BN, Lk);
   };
   auto issue_v = [&](int t) __attribute__((always_inline)) {
-    loader.issue(smem_lds + VBASE + (t % NV) * C::TILEB, Vp, t * BN, Lk);
+    loader.issue(smem_lds + (t % NR) * 2 * C::TILEB + C::TILEB, Vp, t * BN, Lk);
   };
   // Iteration 0 needs K and V tiles 0 and 1 (group A's scores of tile 1);
   // tiles 2 may stay in flight until its end.
@@ -126,10 +127,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
   __syncthreads();
 
   auto k_of = [&](int t) __attribute__((always_inline)) -> const char* {
-    return smem + (t % NK) * C::TILEB;
+    return smem + (t % NR) * 2 * C::TILEB;
   };
   auto v_of = [&](int t) __attribute__((always_inline)) -> const char* {
-    return smem + VBASE + (t % NV) * C::TILEB;
+    return smem + (t % NR) * 2 * C::TILEB + C::TILEB;
   };
   auto scores = [&](const char* kt, const char* vt) __attribute__((always_inline)) {  // S^T, dP^T
 #pragma unroll
@@ -189,8 +190,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
   using Pipe = MfmaReadPipeline<KK * 2 * DD, 2, DS * KK * 2, 1, 4>;
   if (!group_b && ntw > 0) scores(k_of(0), v_of(0));
   for (int t = 0; t < ntiles; ++t) {
-    // K slot (t+3)%5 last served iteration t-1 (K tile t-2, group B's
-    // value); V slot (t+3)%4 last served iteration t-1 (V tile t-1).
+    // Slot (t+3)%5 last served iteration t-1 (K tile t-2, group B's value;
+    // its V tile was last read in iteration t-3).
     if (t + 3 < ntiles) {
       issue_k(t + 3);
       issue_v(t + 3);
