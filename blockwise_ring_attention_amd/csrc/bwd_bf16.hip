@@ -12,7 +12,8 @@
 //     queries and their dO rows in registers and sweeps the block's key /
 //     value tiles through LDS, forming S^T = K Q^T and dP^T = V dO^T (16-byte
 //     LDS reads), dS^T in registers, and dQ^T += K^T dS^T (K^T by LDS
-//     transpose reads).  Eight waves ping-pong as in the forward.
+//     transpose reads).  Eight waves ping-pong as in the forward (group
+//     B's MFMA phase at the higher wave priority).
 //   * dkv_kernel (key-major): a wave keeps 32 keys and their values in
 //     registers and sweeps the query tiles (Q, dO, lse, delta) through LDS,
 //     forming S = Q K^T and dP = dO V^T, then dV += P^T dO and dK += dS^T Q
@@ -40,6 +41,12 @@ struct TileCfg {
   static_assert(STAGEB % (NW * 1024) == 0 && LPW >= 1, "tile must split into 1 KiB loads");
   static_assert(TILEB % 1024 == 0, "a load must not straddle the two tiles");
 };
+
+// Wave priority of group B's MFMA phase in the dQ ping-pong, above group A's
+// (1) and the gradient phases (0): B opens each tile with its MFMA phase, and
+// at equal priority A's MFMA phase, starting when its shorter gradient phase
+// ends, would take the MFMA pipe from B's unfinished one.
+constexpr int kPrioB = 2;
 
 // ---------------------------------------------------------------- dQ ------
 template <int D, int BN, int NW>
@@ -210,13 +217,13 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
       }
     } else {
       if (t >= 1 && t - 1 < ntw) {
-        __builtin_amdgcn_s_setprio(1);
+        __builtin_amdgcn_s_setprio(kPrioB);
         value(k_of(t - 1));
         scores(k_of(t), v_of(t));
         Pipe::apply();
         __builtin_amdgcn_s_setprio(0);
       } else if (t == 0 && ntw > 0) {
-        __builtin_amdgcn_s_setprio(1);
+        __builtin_amdgcn_s_setprio(kPrioB);
         scores(k_of(0), v_of(0));
         __builtin_amdgcn_s_setprio(0);
       }

@@ -36,7 +36,8 @@
 // (the value product of tile t-1 or t and the scores of the next tile) and a
 // VALU phase (softmax of tile t), in opposite orders in the two groups, so
 // the softmax of one wave fills the other wave's MFMA phase.  Both groups
-// meet at one barrier per tile.
+// meet at one barrier per tile.  MFMA phases run at a raised wave priority,
+// group B's (which opens the tile) above group A's.
 //
 // Softmax.  The running max is kept in log2 units (scores scaled by
 // scale*log2(e), folded into the exponent's FMA).  A tile's probabilities
@@ -70,6 +71,12 @@ namespace {
 // A tile's probabilities are taken against the running max as it stands
 // while this lane's share of their sum stays at most kSumLimit.
 constexpr float kSumLimit = 65536.0f;
+
+// Wave priority of group B's MFMA phase, above group A's (1) and the softmax
+// phases (0).  B opens each tile with its MFMA phase; A's softmax is shorter,
+// and at equal priority A's MFMA phase would take the MFMA pipe from B's
+// unfinished one, so that B's softmax later ran with no MFMA work beside it.
+constexpr int kPrioB = 2;
 
 template <int D, int BN, int NW>
 struct FwdCfg {
@@ -299,13 +306,13 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
     } else {
       // B: value(t-1) + scores(t), then softmax(t)
       if (t >= 1 && t - 1 < ntw) {
-        __builtin_amdgcn_s_setprio(1);
+        __builtin_amdgcn_s_setprio(kPrioB);
         value(v_of(t - 1));
         scores(k_of(t));
         Pipe::apply();
         __builtin_amdgcn_s_setprio(0);
       } else if (t == 0 && ntw > 0) {
-        __builtin_amdgcn_s_setprio(1);
+        __builtin_amdgcn_s_setprio(kPrioB);
         scores(k_of(0));
         __builtin_amdgcn_s_setprio(0);
       }
