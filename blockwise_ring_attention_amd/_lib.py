@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libringattn.so")
 
 RA_BF16, RA_FP32 = 0, 1
-RA_EMU_OVERLAP, RA_EMU_SERIALIZE = 0, 1
+RA_EMU_OVERLAP, RA_EMU_SERIALIZE, RA_EMU_UNSAFE = 0, 1, 2
 # RA_DECODE_SCRATCH_BYTES: size of the library's decode scratch array
 DECODE_SCRATCH_BYTES = 16 << 20
 _ERR_NAMES = {-1: "invalid argument", -2: "unsupported", -3: "HIP error"}
@@ -345,9 +345,15 @@ def _order_array(order):
     return arr
 
 
+def _emu_mode(serialize, unsafe):
+    if serialize and unsafe:
+        raise ValueError("serialize and unsafe exclude each other")
+    return RA_EMU_SERIALIZE if serialize else (RA_EMU_UNSAFE if unsafe else RA_EMU_OVERLAP)
+
+
 def ring_emu_fwd(q, kv_pool, slots, ring_rank, ring_size, causal, q_chunk, k_chunk, o_acc,
                  lse_acc, scale=0.0, order=None, serialize=False, main_stream=None,
-                 side_stream=None):
+                 side_stream=None, unsafe=False):
     """kv_pool: list of ring_size packed blocks (None where never needed);
     slots: two receive buffers shaped like one block."""
     if len(kv_pool) != ring_size:
@@ -359,13 +365,13 @@ def ring_emu_fwd(q, kv_pool, slots, ring_rank, ring_size, causal, q_chunk, k_chu
     _check(load().ring_emu_fwd(_ptr(q), _ptr_array(kv_pool), _ptr(slots[0]), _ptr(slots[1]),
                                ring_rank, ring_size, int(bool(causal)), q_chunk, k_chunk,
                                _ptr(o_acc), _ptr(lse_acc), ctypes.byref(dm), _order_array(order),
-                               RA_EMU_SERIALIZE if serialize else RA_EMU_OVERLAP,
+                               _emu_mode(serialize, unsafe),
                                _vp(main.cuda_stream), _vp(side.cuda_stream)))
 
 
 def ring_emu_bwd(q, kv_pool, slots, dout, lse, delta, dkv_pool, dkv_slots, ring_rank, ring_size,
                  causal, q_chunk, k_chunk, dq_acc, scale=0.0, order=None, serialize=False,
-                 main_stream=None, side_stream=None, work=None):
+                 main_stream=None, side_stream=None, work=None, unsafe=False):
     """work: optional device workspace of ring_attn_bwd_workspace bytes."""
     if len(kv_pool) != ring_size or len(dkv_pool) != ring_size:
         raise ValueError("pools must have ring_size entries")
@@ -380,7 +386,7 @@ def ring_emu_bwd(q, kv_pool, slots, dout, lse, delta, dkv_pool, dkv_slots, ring_
                                _ptr(work) if work is not None else None,
                                work.numel() * work.element_size() if work is not None else 0,
                                ctypes.byref(dm), _order_array(order),
-                               RA_EMU_SERIALIZE if serialize else RA_EMU_OVERLAP,
+                               _emu_mode(serialize, unsafe),
                                _vp(main.cuda_stream), _vp(side.cuda_stream)))
 
 

@@ -32,6 +32,11 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wno-inline-as
          "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
+# roctx ranges (ring steps in the emulator) come from the profiler SDK's
+# marker library, part of ROCm.
+LINK = ["-L/opt/rocm/lib", "-lrocprofiler-sdk-roctx"]
+
+
 # Per-source flags.  The backward kernels keep the MFMA results that vector
 # code reads (scores) in VGPRs; their long-lived accumulators are placed in
 # AGPRs explicitly (inline asm), so the MFMA builtins are told to use VGPRs.
@@ -74,7 +79,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:
             f.result()
     tmp = LIB + ".tmp"
-    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
+    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, *LINK, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include <algorithm>
 #include <mutex>
@@ -161,12 +163,21 @@ int ra_block_of_step(int rank, int step, int size) {
   return kb < 0 ? kb + size : kb;
 }
 
+// Diagonal-block mode: 1 skips the tiles wholly above the diagonal; with the
+// environment variable RA_NO_SKIP set (to anything but "0") every tile is
+// computed and masked instead, a debug switch that shows the skip changes no
+// result.  Read at every call, so a process can switch it.
+static int ra_diag_mode() {
+  const char* e = getenv("RA_NO_SKIP");
+  return (e && *e && strcmp(e, "0") != 0) ? 2 : 1;
+}
+
 int ra_fwd_block(const void* q, const void* kv, int kb, int rank, int causal,
                  int q_chunk, int k_chunk, float* o_acc, float* lse_acc,
                  const ra_shape& s, hipStream_t stream) {
   if (s.q_rows == 0 || s.Lk == 0) return RA_OK;  // empty block: identity
   if (causal && kb > rank) return RA_OK;         // entirely in the future
-  ra_launch L{s.B, s.H, s.Lq, s.Lk, s.D, s.Hkv, s.scale, causal && kb == rank ? 1 : 0,
+  ra_launch L{s.B, s.H, s.Lq, s.Lk, s.D, s.Hkv, s.scale, causal && kb == rank ? ra_diag_mode() : 0,
               q_chunk, k_chunk, stream};
   Timed t(s.dtype == RA_BF16 ? kFwdBf16 : kFwdFp32, stream);
   hipError_t e = s.dtype == RA_BF16
@@ -212,7 +223,7 @@ int ra_bwd_block(const void* q, const void* kv, const void* dout, const float* l
                  const ra_shape& s, hipStream_t stream) {
   if (s.q_rows == 0 || s.Lk == 0) return RA_OK;
   if (causal && kb > rank) return RA_OK;
-  ra_launch L{s.B, s.H, s.Lq, s.Lk, s.D, s.Hkv, s.scale, causal && kb == rank ? 1 : 0,
+  ra_launch L{s.B, s.H, s.Lq, s.Lk, s.D, s.Hkv, s.scale, causal && kb == rank ? ra_diag_mode() : 0,
               q_chunk, k_chunk, stream};
   Timed tq(kBwdDq, stream);
   hipError_t e = ra_launch_bwd_dq(q, kv, dout, lse, delta, dq_acc, L);

@@ -85,11 +85,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
   const bf16* Kp = KV + (size_t)kvbh * Lk * D;
   const bf16* Vp = KV + ((size_t)(BH / G) + kvbh) * Lk * D;
 
-  const int kend = diag ? min(Lk, q0 + BM) : Lk;
+  // diag == 2 (no skipping): every tile, the ones above the diagonal fully masked
+  const int kend = diag == 1 ? min(Lk, q0 + BM) : Lk;
   const int ntiles = (kend + BN - 1) / BN;
   const int qw_last = min(qw0 + 31, Lq - 1);
   int ntw = 0;
-  if (qw0 < Lq) ntw = diag ? min(ntiles, qw_last / BN + 1) : ntiles;
+  if (qw0 < Lq) ntw = diag == 1 ? min(ntiles, qw_last / BN + 1) : ntiles;
 
   const LdsOffsets<D> off(lane);
   using Loader = TileLoader<D, BN, NW, false>;
@@ -322,12 +323,13 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
   const float* Dp = Delta + (size_t)bh * Lq;
 
   // Under the causal mask only queries at or after the first key matter.
-  const int qstart = diag ? (k0 / BQ) * BQ : 0;
+  // (diag == 2, no skipping: every query tile, the earlier ones fully masked)
+  const int qstart = diag == 1 ? (k0 / BQ) * BQ : 0;
   const int ntiles = qstart < Lq ? (Lq - qstart + BQ - 1) / BQ : 0;
   const int kw_last = min(kw0 + 31, Lk - 1);
   // This wave's active tiles are a suffix [ft, ntiles): query tiles that
   // end before its first key contribute nothing.
-  int ft = diag ? max(0, (kw0 - qstart) / BQ) : 0;
+  int ft = diag == 1 ? max(0, (kw0 - qstart) / BQ) : 0;
   if (kw0 >= Lk) ft = ntiles;
 
   const LdsOffsets<D> off(lane);

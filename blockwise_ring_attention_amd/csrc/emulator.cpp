@@ -13,10 +13,17 @@
 // On entry the side stream waits for everything already queued on the main
 // stream, so back-to-back calls (a forward share followed by its backward
 // share, or the next step) never overwrite a slot that is still being read.
+// RA_EMU_UNSAFE is a negative control: the consumed[] waits are dropped and
+// each recycled slot is filled with NaN before its next copy, so a step that
+// reads a slot after it was recycled sees poison or another block, and the
+// parity tests show they can tell.  Each compute step is bracketed by a roctx
+// range ("ring fwd|bwd step s: block kb"), visible in a marker trace.
 // Only two slots ever exist, so the member never holds the whole sequence
 // (darcstar commentary: an all-gather of every block would discard the
 // method's memory saving).
 #include <hip/hip_runtime.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
+#include <stdio.h>
 
 #include <vector>
 
@@ -56,6 +63,20 @@ int build_schedule(int rank, int size, int causal, const int32_t* order,
   return RA_OK;
 }
 
+// Host-side roctx range around the enqueue of one ring step.
+struct StepRange {
+  StepRange(const char* pass, int step, int kb) {
+    char name[64];
+    snprintf(name, sizeof name, "ring %s step %d: block %d", pass, step, kb);
+    roctxRangePushA(name);
+  }
+  ~StepRange() { roctxRangePop(); }
+};
+
+bool valid_mode(int mode) {
+  return mode == RA_EMU_OVERLAP || mode == RA_EMU_SERIALIZE || mode == RA_EMU_UNSAFE;
+}
+
 #define RA_HIP(call, what)                             \
   do {                                                 \
     hipError_t _e = (call);                            \
@@ -73,8 +94,7 @@ extern "C" int ring_emu_fwd(const void* q, const void* const* kv_pool, void* slo
   int rc = ra_check_dims(dims, &s);
   if (rc) return rc;
   if ((rc = ra_check_ring(ring_rank, 0, ring_size, causal, q_chunk, k_chunk, s))) return rc;
-  if (mode != RA_EMU_OVERLAP && mode != RA_EMU_SERIALIZE)
-    return ra_fail(RA_ERR_INVALID, "unknown emulator mode %d", mode);
+  if (!valid_mode(mode)) return ra_fail(RA_ERR_INVALID, "unknown emulator mode %d", mode);
   if (!kv_pool) return ra_fail(RA_ERR_INVALID, "kv_pool is NULL");
   std::vector<int> blocks;
   if ((rc = build_schedule(ring_rank, ring_size, causal, order, &blocks))) return rc;
@@ -92,9 +112,12 @@ extern "C" int ring_emu_fwd(const void* q, const void* const* kv_pool, void* slo
   for (int i = 0; i < 2 && i < ncopies; ++i)
     if ((rc = ra_check_fwd_buffers(q, slots[i], o_acc, lse_acc, s))) return rc;
 
+  // async: hops on the side stream ordered by events (overlap, unsafe);
+  // guarded: a slot is recycled only after its compute (overlap).
+  const bool async = mode != RA_EMU_SERIALIZE, guarded = mode == RA_EMU_OVERLAP;
   hipStream_t main = (hipStream_t)main_stream;
-  hipStream_t side = mode == RA_EMU_SERIALIZE ? main : (hipStream_t)side_stream;
-  if (mode == RA_EMU_OVERLAP && side == main)
+  hipStream_t side = async ? (hipStream_t)side_stream : main;
+  if (async && side == main)
     return ra_fail(RA_ERR_INVALID, "overlap mode needs a side stream distinct from main");
 
   // copy index -> block id, in arrival order
@@ -103,7 +126,7 @@ extern "C" int ring_emu_fwd(const void* q, const void* const* kv_pool, void* slo
     if (kb != ring_rank) copy_block.push_back(kb);
 
   Events ev;  // 0,1: copied[slot]; 2,3: consumed[slot]; 4: entry
-  if (mode == RA_EMU_OVERLAP) {
+  if (async) {
     if ((rc = ev.create(5))) return rc;
     // Work already queued on main (an earlier share still reading the slots,
     // the caller's writes to the pool) precedes every hop of this call.
@@ -112,12 +135,14 @@ extern "C" int ring_emu_fwd(const void* q, const void* const* kv_pool, void* slo
   }
   auto issue_copy = [&](int ci) -> int {
     const int slot = ci & 1;
-    if (mode == RA_EMU_OVERLAP && ci >= 2)
+    if (guarded && ci >= 2)
       RA_HIP(hipStreamWaitEvent(side, ev.e[2 + slot], 0), "hipStreamWaitEvent");
+    if (!guarded && async && ci >= 2)
+      RA_HIP(hipMemsetAsync(slots[slot], 0xFF, bytes, side), "poison fill");
     RA_HIP(hipMemcpyAsync(slots[slot], kv_pool[copy_block[ci]], bytes,
                           hipMemcpyDeviceToDevice, side),
            "ring hop copy");
-    if (mode == RA_EMU_OVERLAP) RA_HIP(hipEventRecord(ev.e[slot], side), "hipEventRecord");
+    if (async) RA_HIP(hipEventRecord(ev.e[slot], side), "hipEventRecord");
     return RA_OK;
   };
 
@@ -126,11 +151,12 @@ extern "C" int ring_emu_fwd(const void* q, const void* const* kv_pool, void* slo
   // has been enqueued.  Serialize: each copy is issued just before its use.
   const int nc = (int)copy_block.size();
   int issued = 0;
-  if (mode == RA_EMU_OVERLAP)
+  if (async)
     for (; issued < 2 && issued < nc; ++issued)
       if ((rc = issue_copy(issued))) return rc;
-  int ci = 0;
+  int ci = 0, step = 0;
   for (int kb : blocks) {
+    const StepRange range("fwd", step++, kb);
     const void* src = kv_pool[kb];
     int slot = -1;
     if (kb != ring_rank) {
@@ -146,7 +172,7 @@ extern "C" int ring_emu_fwd(const void* q, const void* const* kv_pool, void* slo
                            s, main)))
       return rc;
     if (slot >= 0) {
-      if (mode == RA_EMU_OVERLAP) {
+      if (async) {
         RA_HIP(hipEventRecord(ev.e[2 + slot], main), "hipEventRecord");
         if (issued < nc && issued == ci + 2) {
           if ((rc = issue_copy(issued))) return rc;
@@ -172,8 +198,7 @@ extern "C" int ring_emu_bwd(const void* q, const void* const* kv_pool, void* slo
   if (s.dtype != RA_BF16)
     return ra_fail(RA_ERR_UNSUPPORTED, "backward is implemented for bf16 inputs only");
   if ((rc = ra_check_ring(ring_rank, 0, ring_size, causal, q_chunk, k_chunk, s))) return rc;
-  if (mode != RA_EMU_OVERLAP && mode != RA_EMU_SERIALIZE)
-    return ra_fail(RA_ERR_INVALID, "unknown emulator mode %d", mode);
+  if (!valid_mode(mode)) return ra_fail(RA_ERR_INVALID, "unknown emulator mode %d", mode);
   if (!kv_pool || !dkv_pool) return ra_fail(RA_ERR_INVALID, "pool is NULL");
   std::vector<int> blocks;
   if ((rc = build_schedule(ring_rank, ring_size, causal, order, &blocks))) return rc;
@@ -220,13 +245,16 @@ extern "C" int ring_emu_bwd(const void* q, const void* const* kv_pool, void* slo
       return rc;
   }
 
+  // async: hops on the side stream ordered by events (overlap, unsafe);
+  // guarded: a slot is recycled only after its compute (overlap).
+  const bool async = mode != RA_EMU_SERIALIZE, guarded = mode == RA_EMU_OVERLAP;
   hipStream_t main = (hipStream_t)main_stream;
-  hipStream_t side = mode == RA_EMU_SERIALIZE ? main : (hipStream_t)side_stream;
-  if (mode == RA_EMU_OVERLAP && side == main)
+  hipStream_t side = async ? (hipStream_t)side_stream : main;
+  if (async && side == main)
     return ra_fail(RA_ERR_INVALID, "overlap mode needs a side stream distinct from main");
 
   Events ev;  // 0,1 copied; 2,3 consumed; 4 side done; 5 entry
-  if (mode == RA_EMU_OVERLAP) {
+  if (async) {
     if ((rc = ev.create(6))) return rc;
     RA_HIP(hipEventRecord(ev.e[5], main), "hipEventRecord");
     RA_HIP(hipStreamWaitEvent(side, ev.e[5], 0), "hipStreamWaitEvent");
@@ -236,20 +264,24 @@ extern "C" int ring_emu_bwd(const void* q, const void* const* kv_pool, void* slo
     const int slot = ci & 1;
     // the previous user of this slot finished its compute and its copy-out
     // was issued earlier on the same (side) stream, so ordering is implied
+    // (unsafe: that copy-out did not wait, and the slot is poisoned first)
+    if (!guarded && async && ci >= 2) {
+      RA_HIP(hipMemsetAsync(slots[slot], 0xFF, kv_bytes, side), "poison fill");
+      RA_HIP(hipMemsetAsync(dslots[slot], 0xFF, dkv_bytes, side), "poison fill");
+    }
     RA_HIP(hipMemcpyAsync(slots[slot], kv_pool[copy_block[ci]], kv_bytes,
                           hipMemcpyDeviceToDevice, side),
            "ring hop copy (kv)");
     RA_HIP(hipMemcpyAsync(dslots[slot], dkv_pool[copy_block[ci]], dkv_bytes,
                           hipMemcpyDeviceToDevice, side),
            "ring hop copy (dkv in)");
-    if (mode == RA_EMU_OVERLAP) RA_HIP(hipEventRecord(ev.e[slot], side), "hipEventRecord");
+    if (async) RA_HIP(hipEventRecord(ev.e[slot], side), "hipEventRecord");
     return RA_OK;
   };
   // Send: the partial, now holding this member's contribution, moves on.
   auto issue_out = [&](int ci) -> int {
     const int slot = ci & 1;
-    if (mode == RA_EMU_OVERLAP)
-      RA_HIP(hipStreamWaitEvent(side, ev.e[2 + slot], 0), "hipStreamWaitEvent");
+    if (guarded) RA_HIP(hipStreamWaitEvent(side, ev.e[2 + slot], 0), "hipStreamWaitEvent");
     RA_HIP(hipMemcpyAsync(dkv_pool[copy_block[ci]], dslots[slot], dkv_bytes,
                           hipMemcpyDeviceToDevice, side),
            "ring hop copy (dkv out)");
@@ -257,11 +289,12 @@ extern "C" int ring_emu_bwd(const void* q, const void* const* kv_pool, void* slo
   };
 
   int issued = 0;
-  if (mode == RA_EMU_OVERLAP)
+  if (async)
     for (; issued < 2 && issued < nc; ++issued)
       if ((rc = issue_in(issued))) return rc;
-  int ci = 0;
+  int ci = 0, step = 0;
   for (int kb : blocks) {
+    const StepRange range("bwd", step++, kb);
     const void* src = kv_pool[kb];
     float* dsrc = dkv_pool[kb];
     int slot = -1;
@@ -279,16 +312,16 @@ extern "C" int ring_emu_bwd(const void* q, const void* const* kv_pool, void* slo
                            dq_acc, dsrc, (float*)work, nsplit, s, main)))
       return rc;
     if (slot >= 0) {
-      if (mode == RA_EMU_OVERLAP) RA_HIP(hipEventRecord(ev.e[2 + slot], main), "hipEventRecord");
+      if (async) RA_HIP(hipEventRecord(ev.e[2 + slot], main), "hipEventRecord");
       if ((rc = issue_out(ci))) return rc;
-      if (mode == RA_EMU_OVERLAP && issued < nc && issued == ci + 2) {
+      if (async && issued < nc && issued == ci + 2) {
         if ((rc = issue_in(issued))) return rc;
         ++issued;
       }
       ++ci;
     }
   }
-  if (mode == RA_EMU_OVERLAP && nc > 0) {
+  if (async && nc > 0) {
     // the caller's main stream completes only after the last hop has landed
     RA_HIP(hipEventRecord(ev.e[4], side), "hipEventRecord");
     RA_HIP(hipStreamWaitEvent(main, ev.e[4], 0), "hipStreamWaitEvent");

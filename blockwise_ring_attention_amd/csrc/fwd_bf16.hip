@@ -122,12 +122,13 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
   const bf16* Kp = KV + (size_t)kvbh * Lk * D;
   const bf16* Vp = KV + ((size_t)(BH / G) + kvbh) * Lk * D;
 
-  const int kend = diag ? min(Lk, q0 + C::BM) : Lk;
+  // diag == 2 (no skipping): every tile, the ones above the diagonal fully masked
+  const int kend = diag == 1 ? min(Lk, q0 + C::BM) : Lk;
   const int ntiles = (kend + BN - 1) / BN;
   // tiles this wave computes: a prefix [0, ntw)
   const int qw_last = min(qw0 + 31, Lq - 1);
   int ntw = 0;
-  if (qw0 < Lq) ntw = diag ? min(ntiles, qw_last / BN + 1) : ntiles;
+  if (qw0 < Lq) ntw = diag == 1 ? min(ntiles, qw_last / BN + 1) : ntiles;
 
   const LdsOffsets<D> off(lane);
 

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kRows) void fwd_fp32_kernel(
     acc[d] = 0.f;
   }
   float m = kNegBig, l = 0.f;
-  const int kend = diag ? min(Lk, q0 + kRows) : Lk;
+  const int kend = diag == 1 ? min(Lk, q0 + kRows) : Lk;  // 2: no skipping
 
   for (int t0 = 0; t0 < kend; t0 += BN) {
     __syncthreads();

@@ -10,7 +10,8 @@ struct ra_launch {
   int B, H, Lq, Lk, D;
   int Hkv;           // key/value heads (divides H)
   float scale;       // resolved (never 0)
-  int diag;          // causal diagonal block: mask key j > query i (local)
+  int diag;          // causal diagonal block: mask key j > query i (local); 1 skips
+                     // tiles wholly above the diagonal, 2 computes them masked
   int q_chunk, k_chunk;
   hipStream_t stream;
 };

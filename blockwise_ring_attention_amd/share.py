@@ -98,20 +98,22 @@ def side_stream_for(device) -> torch.cuda.Stream:
 
 
 def forward(dev: DeviceShare, q_chunk: Optional[int] = None, k_chunk: Optional[int] = None,
-            order=None, serialize: bool = False, side_stream=None) -> None:
-    """Initialise the accumulators and fold every block the member sees."""
+            order=None, serialize: bool = False, side_stream=None, unsafe: bool = False) -> None:
+    """Initialise the accumulators and fold every block the member sees
+    (unsafe: the emulator's race negative control, wrong results on purpose)."""
     cfg = dev.cfg
     if side_stream is None and not serialize:
         side_stream = side_stream_for(dev.q.device)
     _lib.ring_attn_init_acc(dev.o_acc, dev.lse_acc)
     _lib.ring_emu_fwd(dev.q, dev.pool, dev.slots, dev.rank, cfg.ring_size, cfg.causal,
                       q_chunk or cfg.q_chunk, k_chunk or cfg.k_chunk, dev.o_acc, dev.lse_acc,
-                      order=order, serialize=serialize, side_stream=side_stream)
+                      order=order, serialize=serialize, side_stream=side_stream,
+                      unsafe=unsafe)
 
 
 def backward(dev: DeviceShare, q_chunk: Optional[int] = None, k_chunk: Optional[int] = None,
              order=None, serialize: bool = False, side_stream=None,
-             use_work: bool = True) -> None:
+             use_work: bool = True, unsafe: bool = False) -> None:
     """Gradients of the finished forward share: dq_acc, and dkv_pool[kb] +=
     this member's dK/dV contribution for every block it sees.  With shared
     key/value heads the share's workspace (if any) lets query heads of a
@@ -125,7 +127,7 @@ def backward(dev: DeviceShare, q_chunk: Optional[int] = None, k_chunk: Optional[
                       dev.dkv_pool, dev.dkv_slots, dev.rank, cfg.ring_size, cfg.causal,
                       q_chunk or cfg.q_chunk, k_chunk or cfg.k_chunk, dev.dq_acc,
                       order=order, serialize=serialize, side_stream=side_stream,
-                      work=dev.work if use_work else None)
+                      work=dev.work if use_work else None, unsafe=unsafe)
 
 
 def finalize(dev: DeviceShare) -> torch.Tensor:

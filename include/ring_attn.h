@@ -48,6 +48,11 @@
  *   kb = (r - s) mod N (it receives from its predecessor; step 0 is its own
  *   block).  Under the causal mask a block with kb > r is entirely in the
  *   future: the call is a no-op that launches nothing.
+ * - Debug switch: with the environment variable RA_NO_SKIP set (to anything
+ *   but "0") at the time of a call, the causal diagonal block computes every
+ *   tile, the ones wholly above the diagonal fully masked, instead of
+ *   skipping them (ring_attn_fwd, ring_attn_bwd, ring_attn_bwd_ws and the
+ *   emulator).  Results are bitwise those of the skipping path.
  * - Scores are scale * <q_i, k_j> with scale = ra_dims.scale, or 1/sqrt(d)
  *   when ra_dims.scale == 0.  LSE is the natural-log log-sum-exp of the
  *   scores over the keys a row has seen so far.
@@ -329,8 +334,14 @@ int ring_ffn_bwd(const void* x, const void* w1, const void* w2,
  *          ids giving the arrival order (any permutation; the result is
  *          order-invariant because the combine is commutative).
  * mode:    RA_EMU_OVERLAP (side-stream copies) or RA_EMU_SERIALIZE (all on
- *          main_stream; must match OVERLAP bitwise). */
-enum { RA_EMU_OVERLAP = 0, RA_EMU_SERIALIZE = 1 };
+ *          main_stream; must match OVERLAP bitwise), or RA_EMU_UNSAFE, a
+ *          negative control for tests: as OVERLAP but a slot is recycled
+ *          without waiting for the step that reads it and is filled with NaN
+ *          before its next copy, so results are wrong (never a fault: every
+ *          access stays inside the caller's buffers).
+ * Each step's enqueue is bracketed by a roctx range "ring fwd|bwd step s:
+ * block kb" (host side; shown by a profiler's marker trace). */
+enum { RA_EMU_OVERLAP = 0, RA_EMU_SERIALIZE = 1, RA_EMU_UNSAFE = 2 };
 
 int ring_emu_fwd(const void* q, const void* const* kv_pool, void* slot0,
                  void* slot1, int ring_rank, int ring_size, int causal,

@@ -354,11 +354,28 @@ def test_emulator_rejects_bad_schedules(lib):
                           ctypes.c_void_p(0x10000000), ctypes.c_void_p(0x20000000),
                           ctypes.byref(d), None, 5, None, None)
     assert rc == -1 and b"mode" in lib.ring_attn_last_error()
-    # two blocks need a receive slot; none given
+    # two blocks need a receive slot; none given (any valid mode, unsafe too)
+    for mode in (0, 1, 2):
+        rc = lib.ring_emu_fwd(FAKE, pool, None, None, 0, 2, 0, 64, 64,
+                              ctypes.c_void_p(0x10000000), ctypes.c_void_p(0x20000000),
+                              ctypes.byref(d), None, mode, None, None)
+        assert rc == -1 and b"slot" in lib.ring_attn_last_error()
     rc = lib.ring_emu_fwd(FAKE, pool, None, None, 0, 2, 0, 64, 64,
                           ctypes.c_void_p(0x10000000), ctypes.c_void_p(0x20000000),
-                          ctypes.byref(d), None, 0, None, None)
-    assert rc == -1 and b"slot" in lib.ring_attn_last_error()
+                          ctypes.byref(d), None, 3, None, None)
+    assert rc == -1 and b"mode" in lib.ring_attn_last_error()
+
+
+def test_emulator_modes_match_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"enum \{ RA_EMU_OVERLAP = (\d), RA_EMU_SERIALIZE = (\d), RA_EMU_UNSAFE = (\d) \}", text)
+    assert m and tuple(int(x) for x in m.groups()) == (
+        _lib.RA_EMU_OVERLAP, _lib.RA_EMU_SERIALIZE, _lib.RA_EMU_UNSAFE)
+    assert _lib._emu_mode(False, False) == _lib.RA_EMU_OVERLAP
+    assert _lib._emu_mode(True, False) == _lib.RA_EMU_SERIALIZE
+    assert _lib._emu_mode(False, True) == _lib.RA_EMU_UNSAFE
+    with pytest.raises(ValueError):
+        _lib._emu_mode(True, True)
 
 
 def test_bench_trace_overlap_report(tmp_path, capsys):
