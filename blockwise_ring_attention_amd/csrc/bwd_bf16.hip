@@ -419,7 +419,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
     dk[dd] = f32x16{};
     dv[dd] = f32x16{};
   }
-  f32x16 s, dp;               // S and dP of the newest scored sub-tile
+  f32x16 s;                   // S of the newest scored sub-tile
   bf16x8 pbf[2][2], dsbf[2][2];  // P and dS of two sub-tiles ([set][16-query half])
 
   wait_vmem();
@@ -450,8 +450,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
   constexpr int NS = 2 * DS, NP = 4 * DD, LEAD = 4;
   constexpr int EPC = 16 / NP;  // gradient elements per product MFMA
   static_assert(16 % NP == 0, "gradient chunking");
-  // -lse*log2e (nl) and -delta (ndl: the dP accumulators start from it) of
-  // the 16 query rows a lane holds, one set per step of an iteration.
+  // -lse*log2e (nl) and -delta (ndl) of the 16 query rows a lane holds, one
+  // set per step of an iteration.  ndl[qs] is also step qs's dP accumulator:
+  // the dP MFMAs start from -delta in place, and the next rows are loaded
+  // into the other set.
   f32x4 nl[2][4];
   f32x16 ndl[2];
   auto ld_rows = [&](int t, int qs, int g) __attribute__((always_inline)) {  // 1 of 4 read pairs
@@ -496,7 +498,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
     f32x16 pr, dsr;
     u32x4 pw[2], dw[2];
     auto finish = [&](int r) __attribute__((always_inline)) {  // dS and rounding of element r
-      dsr[r] = pr[r] * dp[r];  // dP already holds dO V^T - delta
+      dsr[r] = pr[r] * ndl[qs][r];  // dP already holds dO V^T - delta
       if (r & 1) {
         const bf16x2 pp = {(bf16)pr[r - 1], (bf16)pr[r]};
         const bf16x2 d2 = {(bf16)dsr[r - 1], (bf16)dsr[r]};
@@ -510,7 +512,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkv_kernel(
       if (c < DS) {
         s = mfma32(op[c], kreg[c], c == 0 ? f32x16{} : s);
       } else if (c < NS) {
-        dp = mfma32(op[c], vreg[c - DS], c == DS ? ndl[qs] : dp);
+        ndl[qs] = mfma32(op[c], vreg[c - DS], ndl[qs]);
       } else if (prod) {
         const int i = c - NS, p = i / (2 * DD), dd = (i / 2) % DD;
         if ((i & 1) == 0)
