@@ -167,9 +167,9 @@ def test_causal_independence_bitwise():
 def test_shared_kv_heads_backward(kv_heads, use_work):
     """MQA (one key/value head) and GQA (two, for four query heads): dK/dV of
     a shared head sums its query heads' contributions, element by element
-    against the oracle, with the group's query heads side by side (dK/dV
-    copies in the workspace: 4 for MQA, 2 for GQA here) or one launch per
-    member."""
+    against the oracle, with the group's query heads side by side (4 for
+    MQA, 2 for GQA here: 3 and 1 dK/dV copies in the workspace) or one
+    launch per member."""
     cfg = ShareConfig(98, f"shared-kv{kv_heads}", "bf16", 1, 4, 128, 3, 200, (2,), True,
                       256, 64, backward=True, kv_heads=kv_heads)
     host = share.make_host_share(cfg, 2, seed=8, backward=True)
