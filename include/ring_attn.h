@@ -14,15 +14,16 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - All tensor pointers are DEVICE pointers on the current HIP device.  The
- *   caller allocates and frees every buffer; the library allocates no device
- *   memory (its only device storage is the fixed scratch array of
- *   ring_attn_fwd_decode_noalloc, part of the loaded code object).  All work is enqueued asynchronously on the given hipStream_t
+ *   caller allocates and frees every buffer, workspaces included; the
+ *   library allocates no device memory (its only device storage is the fixed
+ *   scratch array of ring_attn_fwd_decode_noalloc, part of the loaded code
+ *   object).  All work is enqueued asynchronously on the given hipStream_t
  *   (passed as void*; NULL = the null stream); a device fault surfaces at the
  *   caller's next synchronisation.
  * - Every compute entry point (ring_attn_init_acc, ring_attn_fwd,
  *   ring_attn_fwd_decode, ring_attn_fwd_decode_noalloc, ring_attn_combine,
- *   ring_attn_finalize, ring_attn_bwd_prep, ring_attn_bwd, ring_attn_bwd_ws, ring_ffn_fwd,
- *   ring_ffn_bwd) only
+ *   ring_attn_finalize, ring_attn_bwd_prep, ring_attn_bwd, ring_attn_bwd_ws,
+ *   ring_ffn_fwd, ring_ffn_bwd) only
  *   launches kernels on the given stream: no allocation, no hipMemset, no
  *   synchronisation, so a sequence of them may be captured into a HIP graph
  *   and replayed.  Timing (ring_attn_timing_enable) records events and must
