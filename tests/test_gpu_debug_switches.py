@@ -55,6 +55,25 @@ def test_no_skip_is_bitwise(case, monkeypatch):
             assert torch.equal(x, y), f"dkv[{kb}]"
 
 
+def test_no_skip_is_bitwise_fp32_forward(monkeypatch):
+    """The fp32 forward (one query row per thread) under RA_NO_SKIP."""
+    cfg = ShareConfig(92, "fp32 no-skip", "fp32", 1, 2, 64, 3, 200, (2,), True, 64, 64)
+    host = share.make_host_share(cfg, 2, seed=14)
+    outs = []
+    for flag in (None, "1"):
+        if flag is None:
+            monkeypatch.delenv("RA_NO_SKIP", raising=False)
+        else:
+            monkeypatch.setenv("RA_NO_SKIP", flag)
+        dev = share.upload(host)
+        share.forward(dev)
+        torch.cuda.synchronize()
+        outs.append((dev.o_acc.clone(), dev.lse_acc.clone()))
+    monkeypatch.delenv("RA_NO_SKIP")
+    assert torch.isfinite(outs[0][0]).all()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
 def _rel(x, ref):
     return (torch.linalg.vector_norm(x - ref) / torch.linalg.vector_norm(ref)).item()
 
