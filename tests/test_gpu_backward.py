@@ -54,6 +54,10 @@ SMALL = [
     ("d128 causal diagonal only", 1, 2, 128, 2, 256, 0, True),
     ("d64 causal", 1, 2, 64, 4, 96, 3, True),
     ("d128 noncausal", 2, 1, 128, 3, 160, 1, False),
+    # degenerate lengths: one token per block, one row past a 32-row tile
+    ("d128 causal single token", 1, 2, 128, 3, 1, 2, True),
+    ("d128 causal 33 tokens", 1, 2, 128, 2, 33, 1, True),
+    ("d64 noncausal 65 tokens", 1, 1, 64, 2, 65, 0, False),
 ]
 
 

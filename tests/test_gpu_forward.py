@@ -54,6 +54,10 @@ SMALL = [
     ("bf16 d128 diagonal only, three workgroups", "bf16", 1, 2, 128, 2, 600, 0, True, 256, 64),
     ("fp32 d128 causal ragged", "fp32", 1, 2, 128, 3, 100, 2, True, 64, 64),
     ("fp32 d64 noncausal", "fp32", 1, 2, 64, 2, 77, 1, False, 64, 64),
+    # degenerate lengths: one token per block, and one row past a 32-row tile
+    ("bf16 d128 causal single token", "bf16", 1, 2, 128, 3, 1, 2, True, 256, 64),
+    ("bf16 d64 noncausal 33 tokens", "bf16", 1, 2, 64, 2, 33, 1, False, 128, 32),
+    ("fp32 d128 causal single token", "fp32", 1, 1, 128, 2, 1, 1, True, 64, 64),
 ]
 
 
