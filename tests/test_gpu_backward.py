@@ -275,10 +275,11 @@ def test_benchmark_training_share_full_size():
     """The training share the benchmark times (rank 7 of a ring of 8, 16384
     tokens per member, 32 heads of 128, bf16, seed 0), run as the benchmark
     runs it (emulated ring with side-stream hops): dQ on one row of every
-    query tile of every head; dK / dV of one head at keys on block and tile
-    seams of every block, whose gradients need every row of the share (the
-    oracle takes each row's log-sum-exp and delta from a full pass, then
-    only those key columns)."""
+    query tile of every head; dK / dV of four heads at one key of every
+    128-key tile (one dK/dV workgroup each) and at the tile seams of every
+    block, whose gradients need every row of the share (the oracle takes
+    each row's log-sum-exp and delta from a full pass, then only those key
+    columns)."""
     from blockwise_ring_attention_amd.configs import scaled
     cfg = scaled(CONFIGS[3], backward=True)
     rank = cfg.ranks[0]
@@ -291,20 +292,20 @@ def test_benchmark_training_share_full_size():
     print(f"bench share: oracle dq on every tile of {cfg.heads} heads", flush=True)
     _dq_every_tile(host, dev, rng, [0, 1, L - 1])
 
-    h = int(rng.integers(cfg.heads))
     blocks = sorted(host.kv)
-    local = sorted({0, 63, 64, 255, 256, L - 65, L - 64, L - 1} |
-                   set(rng.choice(L, size=2, replace=False).tolist()))
-    keys = [b * L + j for b in blocks for j in local]
-    k = torch.cat([host.kv[b][0][:, [h]] for b in blocks], dim=2)
-    v = torch.cat([host.kv[b][1][:, [h]] for b in blocks], dim=2)
     k_pos = np.concatenate([oracle.positions(b, L) for b in blocks])
-    print(f"bench share: oracle dk/dv of head {h} at {len(keys)} keys", flush=True)
-    dk_ref, dv_ref = oracle.attention_grads_at_keys(
-        host.q[:, [h]], k, v, host.dout[:, [h]], oracle.positions(rank, L), k_pos, True, keys)
-    for i, b in enumerate(blocks):
-        sel = slice(i * len(local), (i + 1) * len(local))
-        got = dev.dkv_pool[b][:, :, [h]][:, :, :, local].cpu()
-        check(f"dk[{b}] h{h}", got[0], dk_ref[:, :, sel], "bf16")
-        check(f"dv[{b}] h{h}", got[1], dv_ref[:, :, sel], "bf16")
+    for h in sorted(rng.choice(cfg.heads, size=4, replace=False).tolist()):
+        local = sorted({0, 63, 64, 255, 256, L - 65, L - 64, L - 1} |
+                       {t + int(rng.integers(128)) for t in range(0, L, 128)})
+        keys = [b * L + j for b in blocks for j in local]
+        k = torch.cat([host.kv[b][0][:, [h]] for b in blocks], dim=2)
+        v = torch.cat([host.kv[b][1][:, [h]] for b in blocks], dim=2)
+        print(f"bench share: oracle dk/dv of head {h} at {len(keys)} keys", flush=True)
+        dk_ref, dv_ref = oracle.attention_grads_at_keys(
+            host.q[:, [h]], k, v, host.dout[:, [h]], oracle.positions(rank, L), k_pos, True, keys)
+        for i, b in enumerate(blocks):
+            sel = slice(i * len(local), (i + 1) * len(local))
+            got = dev.dkv_pool[b][:, :, [h]][:, :, :, local].cpu()
+            check(f"dk[{b}] h{h}", got[0], dk_ref[:, :, sel], "bf16")
+            check(f"dv[{b}] h{h}", got[1], dv_ref[:, :, sel], "bf16")
     assert torch.isfinite(dev.dq_acc).all()
