@@ -32,10 +32,11 @@
 // Ping-pong.  On gfx950 a wave's vector ALU work does not run under its own
 // MFMAs, but work of a second wave on the same SIMD largely does.  With
 // eight waves, each SIMD hosts one wave of group A (waves 0..3) and one of
-// group B (waves 4..7).  Per key tile t, each wave runs an MFMA phase
-// (the value product of tile t-1 or t and the scores of the next tile) and a
-// VALU phase (softmax of tile t), in opposite orders in the two groups, so
-// the softmax of one wave fills the other wave's MFMA phase.  Both groups
+// group B (waves 4..7).  Per key tile t, each wave runs an MFMA phase (the
+// value product of tile t-1 or t and the scores of the next tile; B issues
+// its scores first) and a VALU phase (softmax of tile t), in opposite orders
+// in the two groups, so the softmax of one wave fills the other wave's MFMA
+// phase.  Both groups
 // meet at one barrier per tile.  MFMA phases run at a raised wave priority,
 // group B's (which opens the tile) above group A's.
 //
@@ -207,6 +208,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
   // value: KK*2*DD MFMAs with two transpose reads each; scores: DS*KK MFMAs
   // with one 16-byte read each.
   using Pipe = MfmaReadPipeline<KK * 2 * DD, 2, DS * KK, 1, 4>;
+  using PipeSV = MfmaReadPipeline<DS * KK, 1, KK * 2 * DD, 2, 4>;  // scores first
   // s (raw scores) -> pb = bf16(exp2(s*c2 - m)); returns this lane's share of
   // the row sum of the fp32 probabilities, added in four independent chains.
   auto probs = [&]() __attribute__((always_inline)) -> float {
@@ -305,12 +307,14 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(
         copy1(true, t + 2, 1);
       }
     } else {
-      // B: value(t-1) + scores(t), then softmax(t)
+      // B: scores(t) + value(t-1), then softmax(t).  (Scores first: the
+      // tile then opens with 16-byte K reads; measured 0.3-0.7 % faster than
+      // value first.)
       if (t >= 1 && t - 1 < ntw) {
         __builtin_amdgcn_s_setprio(kPrioB);
-        value(v_of(t - 1));
         scores(k_of(t));
-        Pipe::apply();
+        value(v_of(t - 1));
+        PipeSV::apply();
         __builtin_amdgcn_s_setprio(0);
       } else if (t == 0 && ntw > 0) {
         __builtin_amdgcn_s_setprio(kPrioB);
